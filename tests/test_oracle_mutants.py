@@ -1,0 +1,121 @@
+"""The pins catch planted mistakes (CPU only).
+
+Each case plants one plausible mistake in a copy of an oracle routine --
+a transposed layout index, a dropped scale, a wrong GQA head map, an off-by-one
+causal boundary, a skipped copy-on-write -- and checks that the matching pin
+in test_oracle_pins / test_alloc_model now fails.  The mistakes live only in
+this file and only on the CPU.
+"""
+
+import numpy as np
+import pytest
+
+import oracle.attention as attention
+import oracle.cache as cache
+from oracle.alloc_model import AllocModel
+from tests import test_alloc_model as tam
+from tests import test_oracle_pins as pins
+
+
+def _expect_failure(fn, *args, **kw):
+    with pytest.raises(AssertionError):
+        fn(*args, **kw)
+
+
+def test_transposed_key_layout_is_caught(monkeypatch):
+    def bad_read_key(k_cache, block, head, offset):
+        return k_cache[block, head, :, offset, :].T.reshape(-1)  # d = x * (D/X) + c
+    monkeypatch.setattr(attention, "read_key", bad_read_key)
+    _expect_failure(pins.test_decode_matches_torch_sdpa, "bf16")
+
+
+def test_wrong_offset_in_gather_is_caught(monkeypatch):
+    def bad_read_value(v_cache, block, head, offset):
+        return v_cache[block, head, :, (offset + 1) % v_cache.shape[3]]
+    monkeypatch.setattr(attention, "read_value", bad_read_value)
+    _expect_failure(pins.test_decode_matches_torch_sdpa, "f32")
+
+
+def test_dropped_scale_is_caught(monkeypatch):
+    orig = attention.softmax_weights
+    monkeypatch.setattr(attention, "softmax_weights", lambda q, K, scale: orig(q, K, 1.0))
+    _expect_failure(pins.test_decode_matches_torch_sdpa, "f32")
+
+
+def test_wrong_max_sign_is_caught(monkeypatch):
+    def bad(q, K, scale):
+        s = float(scale) * (K @ q)
+        e = np.exp(-(s - s.max()))
+        return e / e.sum()
+    monkeypatch.setattr(attention, "softmax_weights", bad)
+    _expect_failure(pins.test_decode_matches_torch_sdpa, "f32")
+
+
+def test_wrong_gqa_head_map_is_caught(monkeypatch):
+    orig = attention.gather_kv
+
+    def bad_gather(k_cache, v_cache, bt, L, kv_head, dtype):
+        # serve the other KV head: h % KVH instead of h // group
+        return orig(k_cache, v_cache, bt, L, (kv_head + 1) % k_cache.shape[1], dtype)
+    monkeypatch.setattr(attention, "gather_kv", bad_gather)
+    _expect_failure(pins.test_decode_matches_torch_sdpa, "bf16")
+
+
+def test_causal_off_by_one_is_caught(monkeypatch):
+    orig = attention.attend
+
+    def bad_attend(q, K, V, scale):
+        return orig(q, K[:-1] if K.shape[0] > 1 else K, V[:-1] if V.shape[0] > 1 else V, scale)
+    monkeypatch.setattr(attention, "attend", bad_attend)
+    _expect_failure(pins.test_prefill_matches_torch_sdpa, [0, 0])
+
+
+def test_transposed_value_write_is_caught(monkeypatch):
+    def bad_write(key, value, k_cache, v_cache, slot_mapping):
+        bs, x = k_cache.shape[3], k_cache.shape[4]
+        for i, slot in enumerate(slot_mapping):
+            if slot < 0:
+                continue
+            b, o = int(slot) // bs, int(slot) % bs
+            for g in range(key.shape[1]):
+                k_cache[b, g, :, o, :] = key[i, g].reshape(-1, x)
+                v_cache[b, g, :, o] = value[i, g][::-1]
+    monkeypatch.setattr(cache, "reshape_and_cache", bad_write)
+    _expect_failure(pins.test_cache_layout_offsets, "bf16")
+
+
+def test_skipped_copy_on_write_is_caught(monkeypatch):
+    def bad_append(self, seq, n):
+        bs = self.block_size
+        table = self.tables[seq]
+        L = self.lens[seq]
+        grow = -(-(L + n) // bs) - len(table)
+        if grow > len(self.free):
+            return -2, [], []
+        for _ in range(grow):
+            b = self.free.pop()
+            self.refcount[b] = 1
+            table.append(b)
+        self.lens[seq] = L + n
+        return 0, [table[p // bs] * bs + p % bs for p in range(L, L + n)], []
+    monkeypatch.setattr(AllocModel, "append", bad_append)
+    _expect_failure(tam.test_random_operations_keep_sharing_semantics, 0, 40, 16)
+
+
+def test_fork_without_refcount_is_caught(monkeypatch):
+    def bad_fork(self, parent, child):
+        self.tables[child] = list(self.tables[parent])
+        self.lens[child] = self.lens[parent]
+        return 0
+    monkeypatch.setattr(AllocModel, "fork", bad_fork)
+    _expect_failure(tam.test_random_operations_keep_sharing_semantics, 1, 40, 16)
+
+
+def test_wrong_merge_weight_is_caught(monkeypatch):
+    def bad_partitioned(q_row, K, V, scale, partition):
+        outs = []
+        for a in range(0, K.shape[0], partition):
+            outs.append(attention.attend(q_row, K[a:a + partition], V[a:a + partition], scale))
+        return np.mean(outs, 0)  # forgets the l_p * exp(m_p - M) weights
+    monkeypatch.setattr(attention, "decode_partitioned", bad_partitioned)
+    _expect_failure(pins.test_partition_merge_equals_one_pass, 3)
