@@ -1,0 +1,329 @@
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--configs a,b,...] [--no-cpu-baseline]
+
+Headline workload: batch-64 bf16 decode (32 heads = 32 KV heads, head_dim 128,
+block_size 16, contexts uniform in [512, 2048], blocks scattered at random
+over a pool 1.25x the blocks needed).  One step is one pass of the whole path
+over the batch: the host allocator appends one token per sequence (slot
+mapping, any copy-on-write), slots / block tables / lengths go to the device,
+pa_copy_blocks runs for any copy-on-write, pa_reshape_and_cache writes the new
+tokens' K/V, and pa_decode attends over every context.  Inputs (queries, new
+K/V rows) are resident in HBM before timing starts.
+
+Prints one JSON line.  ``value`` is the decode KV-read rate of the whole step
+(KV bytes the step's attention must read / step wall time); ``roofline`` is
+the pa_decode launch alone, timed with HIP events around each launch on the
+stream it runs on.  The other workloads (GQA long-context decode,
+shared-prefix decode, chunked prefill) are reported under ``workloads``.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+METRIC = "decode KV-read GB/s (% HBM peak), seq-tokens/s; prefill-chunk TFLOP/s (% MFMA)"
+
+
+def kv_bytes(lens, spec) -> int:
+    esz = 2 if spec.dtype == "bf16" else 4
+    return int(np.sum(lens, dtype=np.int64)) * spec.num_kv_heads * spec.head_dim * 2 * esz
+
+
+def unique_kv_bytes(tables, lens, spec) -> int:
+    """KV bytes counting every distinct physical (block, kv head) page's used
+    tokens once (shared prefix pages are read once by the method)."""
+    esz = 2 if spec.dtype == "bf16" else 4
+    used = {}
+    bs = spec.block_size
+    for row, L in zip(tables, lens):
+        for i in range(-(-int(L) // bs)):
+            b = int(row[i])
+            used[b] = max(used.get(b, 0), min(bs, int(L) - i * bs))
+    return sum(used.values()) * spec.num_kv_heads * spec.head_dim * 2 * esz
+
+
+def bench_decode(name: str, steps: int, warmup: int):
+    import torch
+
+    from paged_kv_cache_219_amd.kernels import (decode_workspace, pa_copy_blocks, pa_decode,
+                                                pa_reshape_and_cache)
+    from paged_kv_cache_219_amd.workload import DeviceWorkload, to_device
+    from synth import config_script
+
+    sc = config_script(name)
+    spec = sc.spec
+    dev = torch.device("cuda")
+    w = DeviceWorkload(sc, device=dev, poison=False)
+    B = len(sc.batch)
+    total = warmup + steps
+    if total > 64:
+        raise SystemExit("at most 64 decode steps (table growth reserved by the workload)")
+    # per-step inputs, resident before timing
+    ks, vs, qs = [], [], []
+    step_ops = {op.seq: op for op in sc.step}
+    for i in range(total):
+        if i == 0:
+            kv = [sc.kv(step_ops[s]) for s in sc.batch]
+            k = np.stack([a[0][0] for a in kv])
+            v = np.stack([a[1][0] for a in kv])
+        else:
+            k, v = sc.step_kv(i)
+        ks.append(to_device(k, spec.dtype, dev))
+        vs.append(to_device(v, spec.dtype, dev))
+        qs.append(to_device(sc.q(i), spec.dtype, dev))
+    out = torch.empty_like(qs[0])
+    mb = sc.max_blocks_per_seq
+    lens0 = np.array(sc.notes["context_lens"])
+    max_ctx = int(lens0.max()) + total
+    ws = decode_workspace(B, spec.num_heads, spec.head_dim, max_ctx, spec.partition, dev)
+    seqs = np.array(sc.batch, np.int64)
+    ones = np.ones(B, np.int32)
+    R = 3  # ring of pinned host buffers
+    pin = []
+    for _ in range(R):
+        t_slots = torch.empty(B, dtype=torch.int64, pin_memory=True)
+        t_tab = torch.empty((B, mb), dtype=torch.int32, pin_memory=True)
+        t_len = torch.empty(B, dtype=torch.int32, pin_memory=True)
+        t_cow = torch.empty((B, 2), dtype=torch.int32, pin_memory=True)
+        pin.append((t_slots, t_tab, t_len, t_cow, torch.cuda.Event()))
+    d_slots = torch.empty(B, dtype=torch.int64, device=dev)
+    d_tab = torch.empty((B, mb), dtype=torch.int32, device=dev)
+    d_len = torch.empty(B, dtype=torch.int32, device=dev)
+    d_cow = torch.empty((B, 2), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    dec_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    kv_total = 0
+    uniq_total = 0
+    ncow_total = 0
+    torch.cuda.synchronize()
+    for i in range(total):
+        if i == warmup:
+            torch.cuda.synchronize()
+            wall0 = time.perf_counter()
+            t0.record(stream)
+        t_slots, t_tab, t_len, t_cow, ev = pin[i % R]
+        ev.synchronize()  # the copies that last read this ring slot are done
+        slots, cow, tables, lens = w.alloc.batch_append(
+            seqs, ones, mb, tables_out=t_tab.numpy(), lens_out=t_len.numpy(),
+            slots_out=t_slots.numpy(), cow_out=t_cow.numpy())
+        d_slots.copy_(t_slots, non_blocking=True)
+        d_tab.copy_(t_tab, non_blocking=True)
+        d_len.copy_(t_len, non_blocking=True)
+        if len(cow):
+            d_cow[: len(cow)].copy_(t_cow[: len(cow)], non_blocking=True)
+        ev.record(stream)
+        if len(cow):
+            pa_copy_blocks(w.k_cache, w.v_cache, d_cow[: len(cow)])
+        pa_reshape_and_cache(ks[i], vs[i], w.k_cache, w.v_cache, d_slots)
+        timed = i >= warmup
+        if timed:
+            dec_ev[i - warmup][0].record(stream)
+        pa_decode(out, qs[i], w.k_cache, w.v_cache, d_tab, d_len, spec.scale, spec.partition,
+                  int(lens.max()), ws)
+        if timed:
+            dec_ev[i - warmup][1].record(stream)
+            kv_total += kv_bytes(lens, spec)
+            if name.startswith("shared_prefix"):
+                uniq_total += unique_kv_bytes(tables, lens, spec)
+            ncow_total += len(cow)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = t0.elapsed_time(t1) / steps
+    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in dec_ev]))
+    kv_step = kv_total / steps
+    res = {
+        "workload": name, "batch": B, "heads": spec.num_heads, "kv_heads": spec.num_kv_heads,
+        "head_dim": spec.head_dim, "block_size": spec.block_size, "partition": spec.partition,
+        "ms_per_step": step_ms, "wall_ms_per_step": 1e3 * wall / steps,
+        "kv_bytes_per_step": kv_step,
+        "step_kv_GBs": kv_step / (step_ms * 1e-3) / 1e9,
+        "seq_tokens_per_s": B / (step_ms * 1e-3),
+        "decode_ms": dec_ms,
+        "decode_kv_GBs": kv_step / (dec_ms * 1e-3) / 1e9,
+        "cow_pairs": ncow_total,
+    }
+    res["decode_hbm_frac"] = res["decode_kv_GBs"] / HBM_PEAK_GBS
+    if uniq_total:
+        res["unique_kv_bytes_per_step"] = uniq_total / steps
+        res["decode_unique_kv_GBs"] = uniq_total / steps / (dec_ms * 1e-3) / 1e9
+        res["decode_hbm_frac_unique"] = res["decode_unique_kv_GBs"] / HBM_PEAK_GBS
+    del w, ks, vs, qs, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def prefill_flops(cached, n_q, spec) -> float:
+    """4 * D * H * sum over queries of the attended positions (causal)."""
+    tot = 0
+    for c, n in zip(cached, n_q):
+        tot += n * c + n * (n + 1) // 2
+    return 4.0 * spec.head_dim * spec.num_heads * tot
+
+
+def bench_prefill(name: str, steps: int, warmup: int):
+    import torch
+
+    from paged_kv_cache_219_amd.kernels import pa_prefill_chunk, pa_reshape_and_cache
+    from paged_kv_cache_219_amd.workload import DeviceWorkload, to_device
+    from synth import config_script
+
+    sc = config_script(name)
+    spec = sc.spec
+    dev = torch.device("cuda")
+    w = DeviceWorkload(sc, device=dev, poison=False)
+    slots = w.run_step()  # allocate and write the chunk once
+    bt, lens, _, lens_h = w.batch_tables()
+    qsl = w.query_start_loc()
+    q = w.queries(0)
+    out = torch.empty_like(q)
+    kv = [sc.kv(op) for op in sc.step]
+    k = to_device(np.concatenate([a[0] for a in kv]), spec.dtype, dev)
+    v = to_device(np.concatenate([a[1] for a in kv]), spec.dtype, dev)
+    d_slots = torch.from_numpy(np.concatenate([np.asarray(s, np.int64) for s in slots])).to(dev)
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    max_q = max(sc.query_lens)
+    for i in range(warmup + steps):
+        if i == warmup:
+            torch.cuda.synchronize()
+            t0.record(stream)
+        pa_reshape_and_cache(k, v, w.k_cache, w.v_cache, d_slots)
+        if i >= warmup:
+            ev[i - warmup][0].record(stream)
+        pa_prefill_chunk(out, q, w.k_cache, w.v_cache, bt, qsl, lens, max_q, spec.scale)
+        if i >= warmup:
+            ev[i - warmup][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / steps
+    pf_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    cached = sc.notes["cached"]
+    flops = prefill_flops(cached, sc.query_lens, spec)
+    res = {
+        "workload": name, "seqs": len(sc.batch), "chunk": max_q, "heads": spec.num_heads,
+        "head_dim": spec.head_dim, "cached_tokens": cached,
+        "ms_per_step": step_ms, "prefill_ms": pf_ms, "flops_per_call": flops,
+        "prefill_TFLOPs": flops / (pf_ms * 1e-3) / 1e12,
+        "query_tokens_per_s": sum(sc.query_lens) / (step_ms * 1e-3),
+    }
+    res["prefill_mfma_frac"] = res["prefill_TFLOPs"] / BF16_PEAK_TFLOPS
+    del w
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(budget_s: float = 12.0):
+    """The fp64 numpy oracle on a sample of the headline workload's sequences,
+    single-threaded (BLAS pinned to one thread)."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention, run
+    from synth import config_script
+
+    sc = config_script("decode_bf16")
+    spec = sc.spec
+    lens_all = np.array(sc.notes["context_lens"])
+    done_bytes, elapsed, n = 0, 0.0, 0
+    with threadpool_limits(limits=1):
+        for start in range(0, len(sc.batch), 4):
+            sample = sc.batch[start:start + 4]
+            st = run.build(sc, only_seqs=sample)
+            tables, lens = run.batch_tables(st, sc)
+            idx = [sc.batch.index(s) for s in sample]
+            q = sc.q(0)[idx]
+            t = time.perf_counter()
+            attention.decode(q, st.k_cache, st.v_cache, tables[idx], lens[idx], spec.scale, spec.dtype)
+            elapsed += time.perf_counter() - t
+            done_bytes += kv_bytes(lens[idx], spec)
+            n += len(sample)
+            if elapsed >= budget_s:
+                break
+    return {"value": done_bytes / elapsed / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"decode of the first {n} of {len(lens_all)} sequences of the headline "
+                      f"workload (all {spec.num_heads} heads, {done_bytes / 1e6:.0f} MB of KV), "
+                      f"fp64 numpy oracle with BLAS limited to 1 thread; {elapsed:.1f} s",
+            "seq_tokens_per_s": n / elapsed}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--configs", default="gqa_decode_bf16,shared_prefix_bf16,chunked_prefill_bf16",
+                    help="extra workloads reported under 'workloads' ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}): this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    head = bench_decode("decode_bf16", a.steps, a.warmup)
+    print(f"[bench] decode_bf16: step {head['ms_per_step']:.3f} ms, decode {head['decode_ms']:.3f} ms "
+          f"= {head['decode_kv_GBs']:.0f} GB/s", file=sys.stderr, flush=True)
+    extras = []
+    for name in [c for c in a.configs.split(",") if c]:
+        if "prefill" in name:
+            r = bench_prefill(name, a.steps, a.warmup)
+            print(f"[bench] {name}: {r['prefill_ms']:.3f} ms = {r['prefill_TFLOPs']:.1f} TFLOP/s",
+                  file=sys.stderr, flush=True)
+        else:
+            r = bench_decode(name, a.steps, a.warmup)
+            print(f"[bench] {name}: decode {r['decode_ms']:.3f} ms = {r['decode_kv_GBs']:.0f} GB/s",
+                  file=sys.stderr, flush=True)
+        extras.append(r)
+    cpu = None
+    if not a.no_cpu_baseline:
+        cpu = cpu_baseline()
+        print(f"[bench] cpu oracle: {cpu['value']:.3f} GB/s", file=sys.stderr, flush=True)
+    line = {
+        "metric": METRIC,
+        "value": head["step_kv_GBs"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 K/V/Q, random block placement)",
+        "config": {"workload": "decode_bf16: batch 64, 32 heads = 32 KV heads, head_dim 128, "
+                               "block_size 16, contexts U[512,2048], 1 new token/seq/step",
+                   "global_batch": head["batch"], "partition": head["partition"],
+                   "parallelism": "none (1 GPU)"},
+        "seq_tokens_per_s": head["seq_tokens_per_s"],
+        "roofline": {"bound": "hbm", "achieved": head["decode_kv_GBs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": head["decode_kv_GBs"] / HBM_PEAK_GBS,
+                     "traffic": None, "kernel": "pa_decode",
+                     "algorithmic_bytes_per_launch": head["kv_bytes_per_step"],
+                     "launch_ms": head["decode_ms"]},
+        "cpu_baseline": cpu,
+        "workloads": [head] + extras,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

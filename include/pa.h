@@ -1,0 +1,264 @@
+/*
+ * pa.h -- C ABI of libpa, a paged KV-cache attention library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What it computes.  The KV cache of every sequence is split into logical
+ * blocks of block_size tokens; each logical block lives in a physical block
+ * of a shared pool, and a per-sequence block table maps logical to physical
+ * block indices (page "vLLM PagedAttention chuyên sâu: Phân mảnh bộ nhớ KV
+ * Cache, Prefill theo khối & Prefix Caching", locionic.com -- "the deep-dive
+ * page" below -- section "Tương tự phân trang bộ nhớ ảo").  Attention looks
+ * up each token's physical block in the table, gathers K and V from those
+ * scattered blocks and runs ordinary softmax(q K^T * scale) V on them (same
+ * page, section "Cơ chế PagedAttention").
+ *
+ * Conventions shared by every entry point:
+ *  - Every function returns a pa_status (0 = success, < 0 = error).
+ *  - Kernel entry points take device pointers owned by the caller and a
+ *    hipStream_t passed as void*; they only enqueue work on that stream, never
+ *    synchronise and never allocate device memory.  Host-side argument checks
+ *    run before anything is enqueued; a failed check enqueues nothing.  A
+ *    launch failure is reported as PA_ERR_DEVICE.
+ *  - Values that live in device memory (block-table entries, context
+ *    lengths, slots, query offsets) are preconditions and are not checked:
+ *    every table entry of a logical block below ceil(context_len/block_size)
+ *    lies in [0, num_blocks), 0 <= context_len <= max_blocks_per_seq *
+ *    block_size, slots are < num_blocks * block_size and distinct within one
+ *    call.  Violating them is undefined behaviour (out-of-bounds access).
+ *  - dtype: PA_F32 (float) or PA_BF16 (bfloat16 stored as raw 16-bit).
+ *    Outputs have the dtype of the inputs; accumulation is fp32 and the final
+ *    bf16 rounding is round-to-nearest-even.
+ *  - block_size is 16 (the value every example on the deep-dive page uses);
+ *    head_dim is 64 or 128.  Anything else returns PA_ERR_UNSUPPORTED.
+ *
+ * Cache layout (the pages leave it open).  X = 16 / sizeof(element)
+ * (8 for bf16, 4 for fp32):
+ *    k_cache[num_blocks][num_kv_heads][head_dim / X][block_size][X]
+ *    v_cache[num_blocks][num_kv_heads][head_dim][block_size]
+ * Key element (block b, kv head g, offset o, dim d) is
+ * k_cache[b][g][d / X][o][d % X]; the value element is v_cache[b][g][d][o].
+ * A slot is a flat token position in the pool: block * block_size + offset.
+ *
+ * Grouped-query attention: query head h reads KV head h / (num_heads /
+ * num_kv_heads); num_heads must be a multiple of num_kv_heads.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1,    /* null pointer, negative size, inconsistent shapes */
+  PA_ERR_NO_FREE_BLOCKS = -2, /* allocator: the pool cannot satisfy the request */
+  PA_ERR_UNKNOWN_SEQ = -3,    /* allocator: no sequence with that id */
+  PA_ERR_SEQ_EXISTS = -4,     /* allocator: the id is already in use */
+  PA_ERR_UNSUPPORTED = -5,    /* a shape/dtype this build has no kernel for */
+  PA_ERR_WORKSPACE = -6,      /* workspace missing or smaller than required */
+  PA_ERR_DEVICE = -7          /* a HIP call or kernel launch failed */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* pa_status_str(int status);
+
+/* ABI version of this library; bumped on any incompatible change. */
+int pa_version(void);
+
+/* ------------------------------------------------------------------ kernels */
+
+/*
+ * pa_reshape_and_cache -- write new tokens' K and V into their cache slots.
+ *
+ * New tokens of a growing sequence are stored in the physical blocks the
+ * allocator mapped for them, without moving earlier tokens (deep-dive page,
+ * section "Tương tự phân trang bộ nhớ ảo", dynamic resizing; section "Cơ chế
+ * của Chunked Prefill", step 3: a chunk's KV accumulates in blocks the block
+ * manager provides).
+ *
+ *   key, value    device, [num_tokens][num_kv_heads][head_dim], dtype; token i
+ *                 starts at element i * key_stride (resp. value_stride), heads
+ *                 are contiguous (stride head_dim).  strides >= num_kv_heads *
+ *                 head_dim.
+ *   k_cache, v_cache  device, the pool in the layout above (num_blocks blocks).
+ *   slot_mapping  device int64 [num_tokens]; token i goes to slot
+ *                 slot_mapping[i]; a negative slot skips the token.
+ * Bit-exact copy: no value is changed.  num_tokens == 0 enqueues nothing.
+ */
+int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                         const int64_t* slot_mapping, int32_t num_tokens, int64_t key_stride,
+                         int64_t value_stride, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, int32_t dtype, void* stream);
+
+/*
+ * pa_copy_blocks -- copy-on-write block copies.
+ *
+ * A sequence about to write into a physical block it shares first gets a
+ * private copy of that block (deep-dive page, section "Cơ chế APC", item 3).
+ * For each pair p, the whole physical block pairs[2p] (all KV heads, all
+ * offsets, K and V) is copied to block pairs[2p+1].
+ *   pairs  device int32 [num_pairs][2] (src, dst); no dst may appear twice or
+ *          also appear as a src in the same call (the copies run in parallel).
+ * Bit-exact.  num_pairs == 0 enqueues nothing.
+ */
+int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                   int32_t dtype, void* stream);
+
+/*
+ * pa_decode_workspace_bytes -- bytes of device workspace pa_decode needs.
+ * Zero when no sequence can span more than one partition.  Partials are fp32:
+ * num_seqs * num_heads * ceil(max_context_len / partition) * (head_dim + 2)
+ * values, plus alignment.
+ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition);
+
+/*
+ * pa_decode -- one query token per sequence against its paged context.
+ *
+ * For sequence s and query head h (kv head g = h / (num_heads/num_kv_heads)),
+ * with L = context_lens[s], token t in [0, L) is read from physical block
+ * block_tables[s][t / block_size] at offset t % block_size; the output is
+ * sum_t softmax_t(scale * <q[s][h], K_t>) V_t (deep-dive page, section "Cơ chế
+ * PagedAttention", steps 1-3).  L counts every attended token, including the
+ * token written in the same step.  L == 0 gives a zero row.
+ *
+ *   out, q         device [num_seqs][num_heads][head_dim], dtype.
+ *   block_tables   device int32 [num_seqs][max_blocks_per_seq] (row-major,
+ *                  entries past a sequence's last block are ignored; -1 is
+ *                  the conventional padding).
+ *   context_lens   device int32 [num_seqs].
+ *   partition      split-context partition size in tokens: 0 = one pass per
+ *                  (sequence, head); otherwise a positive multiple of 64.  A
+ *                  sequence longer than one partition is processed by
+ *                  ceil(L/partition) independent workgroups whose partial
+ *                  (max, sum, output) triples are merged by a second kernel
+ *                  with log-sum-exp weights.  The result does not depend on
+ *                  the partition size beyond fp32 rounding.
+ *   max_context_len  host upper bound of context_lens (sizes the grid).
+ *   workspace      device scratch of at least pa_decode_workspace_bytes(...)
+ *                  bytes (may be NULL when that is 0); contents on entry are
+ *                  ignored, contents on exit are unspecified.
+ * Deterministic: the reduction order depends only on logical positions, so
+ * results do not depend on block placement or on which blocks are shared.
+ */
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, int32_t max_blocks_per_seq,
+              const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+              int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+              float scale, int32_t partition, int32_t max_context_len, void* workspace,
+              size_t workspace_bytes, int32_t dtype, void* stream);
+
+/*
+ * pa_prefill_chunk -- causal attention of a chunk of query tokens per
+ * sequence against that sequence's paged context (chunked prefill: the
+ * prompt is processed in chunks whose KV accumulates in the cache, deep-dive
+ * page, section "Cơ chế của Chunked Prefill", steps 1-3).
+ *
+ * Sequence s owns query rows query_start_loc[s] .. query_start_loc[s+1]-1
+ * (n_q rows); context_lens[s] = L counts the cached tokens plus this chunk,
+ * whose K/V must already be in the cache.  Query i of the chunk sits at
+ * position L - n_q + i and attends to positions 0 .. L - n_q + i.
+ *
+ *   out, q           device [total_query_rows][num_heads][head_dim], bf16.
+ *   query_start_loc  device int32 [num_seqs + 1], non-decreasing, [0] = 0.
+ *   max_query_len    host upper bound of n_q (sizes the grid).
+ * bf16 only (matrix-core path); PA_F32 returns PA_ERR_UNSUPPORTED.
+ */
+int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* query_start_loc, const int32_t* context_lens, int32_t num_seqs,
+                     int32_t max_query_len, int32_t num_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                     int32_t dtype, void* stream);
+
+/* ---------------------------------------------------------- block allocator */
+
+/*
+ * Host-side block allocator: logical-to-physical block tables, a free list,
+ * per-block reference counts for blocks shared between sequences, and
+ * copy-on-write (deep-dive page, sections "Tương tự phân trang bộ nhớ ảo" and
+ * "Cơ chế APC"; the skymod.tech overview: in parallel sampling the prompt's
+ * memory is shared by the output sequences).  It owns host memory only and
+ * never touches the device: a copy-on-write it decides is returned to the
+ * caller, who enqueues pa_copy_blocks before writing the new tokens.  Not
+ * thread-safe: one scheduler thread drives it.  Every call either succeeds
+ * completely or changes nothing.
+ *
+ * Policies: the free list is a LIFO stack, free_order[0] handed out first;
+ * released blocks are pushed on top, a sequence's blocks from its last
+ * logical block to its first.  fork gives the child the parent's table and
+ * length, each block one more reference.  append of n tokens to a sequence of
+ * length L: if L % block_size != 0 and the last block has more than one
+ * reference, that block is copied first (a fresh block dst replaces src in the
+ * table, src loses one reference, (src, dst) is reported); then
+ * ceil((L+n)/block_size) - blocks_held blocks are popped in logical order, and
+ * the slots of positions L .. L+n-1 are
+ *   slot(p) = table[p / block_size] * block_size + p % block_size.
+ */
+typedef struct pa_allocator pa_allocator;
+
+/* free_order: NULL (identity order) or a permutation of [0, num_blocks). */
+int pa_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                    pa_allocator** out);
+void pa_alloc_destroy(pa_allocator* a);
+
+int pa_seq_new(pa_allocator* a, int64_t seq);
+int pa_seq_fork(pa_allocator* a, int64_t parent, int64_t child);
+/* slots_out: [n] (may be NULL when n == 0); cow_pair_out: [2]; *n_cow_out is
+ * 0 or 1. */
+int pa_seq_append(pa_allocator* a, int64_t seq, int32_t n, int64_t* slots_out,
+                  int32_t* cow_pair_out, int32_t* n_cow_out);
+int pa_seq_free(pa_allocator* a, int64_t seq);
+int pa_seq_len(const pa_allocator* a, int64_t seq, int32_t* len_out);
+/* Copies up to cap entries of the block table; *n_out = the table's length. */
+int pa_seq_block_table(const pa_allocator* a, int64_t seq, int32_t* out, int32_t cap,
+                       int32_t* n_out);
+int pa_block_refcount(const pa_allocator* a, int32_t block, int32_t* rc_out);
+int pa_num_free(const pa_allocator* a, int32_t* n_out);
+/* Copies the free list, bottom of the stack first; *n_out = its length. */
+int pa_free_list(const pa_allocator* a, int32_t* out, int32_t cap, int32_t* n_out);
+
+/*
+ * pa_batch_append -- one decode/prefill step's worth of appends in one call.
+ * Appends n[i] tokens to seqs[i] for i = 0 .. num_seqs-1, in order, each as
+ * pa_seq_append would.  Stops at the first failing append: *n_done_out tells
+ * how many succeeded (those stay applied); the status is that failure's.
+ *   slots_out      [sum n] slots, sequence after sequence.
+ *   cow_pairs_out  [num_seqs][2]; *n_cow_out pairs are written, in order.
+ * Then, on success, exports the batch for the kernels:
+ *   block_tables_out [num_seqs][max_blocks_per_seq] (-1 padded), and
+ *   context_lens_out [num_seqs] (either may be NULL to skip).
+ * A table wider than max_blocks_per_seq returns PA_ERR_INVALID_ARG after the
+ * appends are applied.
+ */
+int pa_batch_append(pa_allocator* a, const int64_t* seqs, int32_t num_seqs, const int32_t* n,
+                    int64_t* slots_out, int32_t* cow_pairs_out, int32_t* n_cow_out,
+                    int32_t* block_tables_out, int32_t max_blocks_per_seq,
+                    int32_t* context_lens_out, int32_t* n_done_out);
+
+/* Block tables and context lengths of seqs[0..num_seqs) as above. */
+int pa_export_tables(const pa_allocator* a, const int64_t* seqs, int32_t num_seqs,
+                     int32_t* block_tables_out, int32_t max_blocks_per_seq,
+                     int32_t* context_lens_out);
+
+/*
+ * pa_alloc_stats -- out[0] free blocks, out[1] blocks in use, out[2] blocks
+ * with more than one reference, out[3] live sequences, out[4] wasted slots
+ * (internal fragmentation: sum over sequences of blocks_held * block_size -
+ * length; below block_size per sequence).
+ */
+int pa_alloc_stats(const pa_allocator* a, int64_t out[5]);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -26,8 +26,10 @@ class OracleState:
     cow_pairs: list = field(default_factory=list)  # every (src, dst) reported
 
 
-def apply_op(st: OracleState, script, op) -> list:
-    """Run one allocator operation; returns the slots of an append."""
+def apply_op(st: OracleState, script, op, write_seqs=None) -> list:
+    """Run one allocator operation; returns the slots of an append.  With
+    ``write_seqs`` given, only appends of those sequences write K/V (the
+    allocator still sees every operation, so placement is unchanged)."""
     slots = []
     if op.kind == "new":
         rc = st.model.new(op.seq)
@@ -39,8 +41,9 @@ def apply_op(st: OracleState, script, op) -> list:
             if pairs:
                 cache.copy_blocks(st.k_cache, st.v_cache, pairs)
                 st.cow_pairs.extend(pairs)
-            k, v = script.kv(op)
-            cache.reshape_and_cache(k, v, st.k_cache, st.v_cache, np.asarray(slots, np.int64))
+            if write_seqs is None or op.seq in write_seqs:
+                k, v = script.kv(op)
+                cache.reshape_and_cache(k, v, st.k_cache, st.v_cache, np.asarray(slots, np.int64))
     else:
         raise ValueError(op.kind)
     if rc != OK:
@@ -48,16 +51,33 @@ def apply_op(st: OracleState, script, op) -> list:
     return slots
 
 
-def build(script, include_step: bool = True, poison: int | None = None) -> OracleState:
+def ancestors(script, seqs) -> set:
+    """``seqs`` plus every sequence they were forked from."""
+    parent = {op.seq: op.parent for op in script.ops() if op.kind == "fork"}
+    out = set()
+    for s in seqs:
+        while s not in out:
+            out.add(s)
+            if s not in parent:
+                break
+            s = parent[s]
+    return out
+
+
+def build(script, include_step: bool = True, poison: int | None = None,
+          only_seqs=None) -> OracleState:
+    """Execute the script.  ``only_seqs`` limits the cache writes to the
+    tokens those sequences (and the sequences they forked from) read."""
     s = script.spec
+    write = None if only_seqs is None else ancestors(script, only_seqs)
     st = OracleState(AllocModel(script.num_blocks, s.block_size, script.free_order),
                      *cache.empty_cache(script.num_blocks, s.num_kv_heads, s.head_dim,
                                         s.block_size, s.dtype, poison))
     for op in script.setup:
-        apply_op(st, script, op)
+        apply_op(st, script, op, write)
     if include_step:
         for op in script.step:
-            st.step_slots.append(apply_op(st, script, op))
+            st.step_slots.append(apply_op(st, script, op, write))
     return st
 
 

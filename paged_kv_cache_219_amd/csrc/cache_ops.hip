@@ -1,0 +1,125 @@
+// Cache writes of libpa: scatter new tokens' K/V into their slots, and copy
+// whole blocks for copy-on-write.  Pure data movement (bit-exact).
+//
+// Page "vLLM PagedAttention chuyên sâu: Phân mảnh bộ nhớ KV Cache, Prefill
+// theo khối & Prefix Caching" (locionic.com): section "Tương tự phân trang bộ
+// nhớ ảo" (new tokens land in newly mapped physical blocks, nothing moves),
+// section "Cơ chế của Chunked Prefill" step 3 (a chunk's KV accumulates in
+// the blocks the block manager hands out), section "Cơ chế APC" item 3
+// (copy-on-write of a shared block before a diverging write).
+//
+// Layout (see include/pa.h): k_cache[NB][KVH][D/X][BS][X] with X elements per
+// 16-byte chunk, v_cache[NB][KVH][D][BS].
+
+#include "pa_device.h"
+
+namespace {
+
+// One wave per (token, kv head).  Lanes copy the key row as 16-byte chunks
+// (each chunk is one x-packed group of the key layout) and the value row
+// element by element into its d-major page.
+template <int ESIZE>
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+    const uint8_t* __restrict__ key, const uint8_t* __restrict__ value, uint8_t* __restrict__ kc,
+    uint8_t* __restrict__ vc, const int64_t* __restrict__ slots, int32_t num_tokens,
+    int64_t kstride_bytes, int64_t vstride_bytes, int32_t kvh, int32_t head_dim,
+    int32_t block_size) {
+  typedef typename std::conditional<ESIZE == 2, uint16_t, uint32_t>::type elem_t;
+  const int lane = threadIdx.x & 63;
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int64_t tok = w / kvh;
+  const int head = static_cast<int>(w % kvh);
+  if (tok >= num_tokens) return;
+  const int64_t slot = slots[tok];
+  if (slot < 0) return;
+  const int64_t blk = slot / block_size;
+  const int off = static_cast<int>(slot % block_size);
+  const int nchunk = head_dim * ESIZE / 16;
+  const uint8_t* ksrc = key + tok * kstride_bytes + static_cast<int64_t>(head) * head_dim * ESIZE;
+  uint8_t* kdst = kc + ((blk * kvh + head) * nchunk * block_size + off) * 16;
+  for (int c = lane; c < nchunk; c += 64) {
+    uint4 v = *reinterpret_cast<const uint4*>(ksrc + c * 16);
+    *reinterpret_cast<uint4*>(kdst + static_cast<int64_t>(c) * block_size * 16) = v;
+  }
+  const elem_t* vsrc = reinterpret_cast<const elem_t*>(value + tok * vstride_bytes) +
+                       static_cast<int64_t>(head) * head_dim;
+  elem_t* vdst = reinterpret_cast<elem_t*>(vc) + (blk * kvh + head) * head_dim * block_size + off;
+  for (int d = lane; d < head_dim; d += 64) vdst[static_cast<int64_t>(d) * block_size] = vsrc[d];
+}
+
+// grid (num_pairs, ceil(units / 256)); each thread copies one 16-byte unit of
+// the K block and one of the V block.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ kc,
+                                                          uint4* __restrict__ vc,
+                                                          const int32_t* __restrict__ pairs,
+                                                          int64_t units_per_block) {
+  const int64_t u = static_cast<int64_t>(blockIdx.y) * blockDim.x + threadIdx.x;
+  if (u >= units_per_block) return;
+  const int64_t src = pairs[2 * blockIdx.x];
+  const int64_t dst = pairs[2 * blockIdx.x + 1];
+  kc[dst * units_per_block + u] = kc[src * units_per_block + u];
+  vc[dst * units_per_block + u] = vc[src * units_per_block + u];
+}
+
+int esize_of(int32_t dtype) { return dtype == PA_BF16 ? 2 : (dtype == PA_F32 ? 4 : 0); }
+
+}  // namespace
+
+extern "C" int pa_reshape_and_cache(const void* key, const void* value, void* k_cache,
+                                    void* v_cache, const int64_t* slot_mapping, int32_t num_tokens,
+                                    int64_t key_stride, int64_t value_stride, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                    int32_t dtype, void* stream) {
+  const int es = esize_of(dtype);
+  if (es == 0) return PA_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (block_size != 16) return PA_ERR_UNSUPPORTED;
+  const int64_t row = static_cast<int64_t>(num_kv_heads) * head_dim;
+  if (key_stride < row || value_stride < row) return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(key) | reinterpret_cast<uintptr_t>(k_cache)) & 15)
+    return PA_ERR_INVALID_ARG;
+  if (((key_stride * es) & 15) != 0) return PA_ERR_INVALID_ARG;
+  const int64_t waves = static_cast<int64_t>(num_tokens) * num_kv_heads;
+  const int64_t blocks = (waves + 3) / 4;
+  if (blocks > 0x7fffffff) return PA_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (es == 2)
+    hipLaunchKernelGGL(reshape_and_cache_kernel<2>, dim3(static_cast<uint32_t>(blocks)), dim3(256),
+                       0, s, static_cast<const uint8_t*>(key), static_cast<const uint8_t*>(value),
+                       static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache),
+                       slot_mapping, num_tokens, key_stride * es, value_stride * es, num_kv_heads,
+                       head_dim, block_size);
+  else
+    hipLaunchKernelGGL(reshape_and_cache_kernel<4>, dim3(static_cast<uint32_t>(blocks)), dim3(256),
+                       0, s, static_cast<const uint8_t*>(key), static_cast<const uint8_t*>(value),
+                       static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache),
+                       slot_mapping, num_tokens, key_stride * es, value_stride * es, num_kv_heads,
+                       head_dim, block_size);
+  return pa_launch_status();
+}
+
+extern "C" int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs,
+                              int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int32_t num_blocks, int32_t dtype, void* stream) {
+  const int es = esize_of(dtype);
+  if (es == 0) return PA_ERR_UNSUPPORTED;
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (block_size != 16) return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !pairs) return PA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache)) & 15)
+    return PA_ERR_INVALID_ARG;
+  const int64_t units = static_cast<int64_t>(num_kv_heads) * head_dim * block_size * es / 16;
+  const int64_t gy = (units + 255) / 256;
+  if (gy > 65535) return PA_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, static_cast<uint32_t>(gy)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<uint4*>(k_cache),
+                     static_cast<uint4*>(v_cache), pairs, units);
+  return pa_launch_status();
+}

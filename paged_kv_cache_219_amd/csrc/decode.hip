@@ -1,0 +1,465 @@
+// Decode attention over a paged KV cache (gfx950, wave64, no matrix cores).
+//
+// Page "vLLM PagedAttention chuyên sâu: Phân mảnh bộ nhớ KV Cache, Prefill
+// theo khối & Prefix Caching" (locionic.com), section "Cơ chế PagedAttention":
+// per query token the kernel (1) looks up the sequence's physical blocks in
+// its block table, (2) gathers K and V from those scattered blocks and (3) runs
+// ordinary attention on them.  Section "Chunked Prefill" states decode is
+// bound by memory bandwidth: the design goal is to stream every K/V page once
+// at HBM speed.
+//
+// Work decomposition.  One wave (one 64-thread workgroup) per (partition,
+// kv head, sequence).  A partition is a run of `partition` tokens (a multiple
+// of 64); a sequence spanning several partitions is processed by independent
+// waves that each emit (m, l, o) -- running max (log2 units), sum of
+// exponentials and normalised partial output -- and a second kernel merges
+// them with weights l_p * 2^(m_p - max m).  The wave walks its partition in
+// tiles of 64 tokens = 4 pages of 16 tokens, prefetching the next tile's
+// block ids, keys and values while it computes on the current one.
+//
+// Within a tile:
+//  * QK, one token per lane: lane 16j+t owns token t of page j and loads that
+//    token's whole key row -- with the x-packed key layout the 16 lanes of a
+//    page read 256 contiguous bytes per load.  The G query heads sharing the
+//    kv head are broadcast from LDS; bf16 products use v_dot2_f32_bf16 (exact
+//    products, fp32 accumulation), so no cross-lane reduction is needed for
+//    the dot products.
+//  * online softmax per head: wave max -> rescale factor 2^(m_old - m_new),
+//    per-lane partial sums of 2^(s - m) (reduced once at the end).
+//  * PV, one value d-row per lane group: with the d-major value page a 16-byte
+//    load holds X consecutive tokens of one dimension, so bf16 weights pair up
+//    with values for v_dot2_f32_bf16 (G >= 4) or are widened to fp32 (G < 4).
+//    The weights go through LDS (64 tokens x G heads).
+// Tokens past the context are masked by selecting -inf scores and zeroing
+// their value elements (the cache may hold anything there).
+
+#include "pa_device.h"
+
+namespace {
+
+constexpr int kBS = 16;
+constexpr int kTile = 64;
+
+template <typename T, int D>
+struct Geo {
+  static constexpr int E = sizeof(T);
+  static constexpr int X = 16 / E;          // elements per 16-byte chunk
+  static constexpr int NKC = D / X;         // key chunks per token row
+  static constexpr int LPR = kBS / X;       // lanes per value d-row (one row = 16 tokens)
+  static constexpr int DPI = 64 / LPR;      // value d-rows covered by one wave load
+  static constexpr int NVI = D / DPI;       // wave loads per value page
+  static constexpr int PAGE = D * kBS;      // elements per (block, kv head) page
+};
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+template <typename T>
+__device__ __forceinline__ void store_out(T* p, float v);
+template <>
+__device__ __forceinline__ void store_out<float>(float* p, float v) { *p = v; }
+template <>
+__device__ __forceinline__ void store_out<uint16_t>(uint16_t* p, float v) {
+  *p = static_cast<uint16_t>(pa::f32_to_bf16_bits(v));
+}
+
+// Zero the elements of a 16-byte value chunk whose token index (0..X-1 within
+// the chunk) is >= keep.
+template <typename T>
+__device__ __forceinline__ uint4 mask_chunk(uint4 v, int keep) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  if (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t m = (2 * i < keep ? 0x0000ffffu : 0u) | (2 * i + 1 < keep ? 0xffff0000u : 0u);
+      w[i] &= m;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = i < keep ? w[i] : 0u;
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <typename T, int D, int G, bool PVB>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_partition_kernel(
+    T* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
+    const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
+    const int32_t* __restrict__ block_tables, int32_t max_blocks,
+    const int32_t* __restrict__ context_lens, int32_t num_heads, int32_t num_kv_heads,
+    int32_t num_parts, int32_t partition, float scale_log2) {
+  using Gm = Geo<T, D>;
+  constexpr int X = Gm::X, NKC = Gm::NKC, LPR = Gm::LPR, DPI = Gm::DPI, NVI = Gm::NVI;
+  typedef typename std::conditional<PVB, uint16_t, float>::type p_t;
+
+  __shared__ __attribute__((aligned(16))) p_t p_lds[G * kTile];
+
+  const int lane = threadIdx.x;
+  const int part = blockIdx.x;
+  const int g = blockIdx.y;
+  const int s = blockIdx.z;
+  const int h0 = g * G;
+  const int L = context_lens[s];
+  const int part_start = part * partition;
+  const int64_t out_row = (static_cast<int64_t>(s) * num_heads + h0) * D;
+
+  if (L <= 0) {
+    if (part == 0)
+      for (int i = lane; i < G * D; i += 64) store_out<T>(out + out_row + i, 0.f);
+    return;
+  }
+  if (part_start >= L) return;
+  const int part_end = min(part_start + partition, L);
+  const int nparts_s = (L + partition - 1) / partition;
+
+  // The G query rows (contiguous) are read-only and wave-uniform: reading them
+  // through the constant address space turns them into scalar loads whose
+  // SGPRs feed the dot products directly.
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const __attribute__((address_space(4))) u32x4* q_const =
+      (const __attribute__((address_space(4))) u32x4*)(q + out_row);
+
+  const int32_t* bt_row = block_tables + static_cast<int64_t>(s) * max_blocks;
+  const int64_t head_off = static_cast<int64_t>(g) * Gm::PAGE;
+  const int64_t blk_stride = static_cast<int64_t>(num_kv_heads) * Gm::PAGE;
+  const int j_me = lane >> 4;   // page of this lane's token (QK layout)
+  const int t_me = lane & 15;   // token within that page
+  const int vrow = lane / LPR;  // value d-row within a wave load
+  const int vtok = X * (lane % LPR);  // first token of this lane's value chunk
+
+  uint4 kreg[NKC];
+  uint4 vreg[4][NVI];
+  float m[G], l[G], acc[G][NVI];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int k = 0; k < NVI; ++k) acc[h][k] = 0.f;
+  }
+
+  const int ntiles = (part_end - part_start + kTile - 1) / kTile;
+  const int lb_part = part_start / kBS;
+
+  // Per-lane block id of the lane's own page, and validity of the 4 pages.
+  auto page_id = [&](int tile, int j) -> int {
+    const int lb = lb_part + tile * 4 + j;
+    return lb * kBS < part_end ? bt_row[lb] : -1;
+  };
+  auto load_k = [&](int phys) {
+    if (phys >= 0) {
+      const T* base = kc + phys * blk_stride + head_off + t_me * X;
+#pragma unroll
+      for (int c = 0; c < NKC; ++c) kreg[c] = ld16(base + c * (kBS * X));
+    } else {
+#pragma unroll
+      for (int c = 0; c < NKC; ++c) kreg[c] = make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto load_v = [&](const int (&ids)[4]) {
+    int vofs = lane * X;
+    // pins the value loads here: the scheduler may not lift them above the
+    // score loop (whose chunk barriers are also volatile)
+    if (G > 2) asm volatile("" : "+v"(vofs));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (ids[j] >= 0) {
+        const T* base = vc + ids[j] * blk_stride + head_off + vofs;
+#pragma unroll
+        for (int k = 0; k < NVI; ++k) vreg[j][k] = ld16(base + k * 64 * X);
+      } else {
+#pragma unroll
+        for (int k = 0; k < NVI; ++k) vreg[j][k] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+
+  int next_id = page_id(0, j_me);
+
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int tile_start = part_start + tile * kTile;
+    const int my_id = next_id;
+    int ids[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ids[j] = __builtin_amdgcn_readlane(my_id, 16 * j);
+    // Issue the whole tile's keys and values at once; other waves on the SIMD
+    // compute while these are in flight.  Only the block ids of the next tile
+    // are fetched ahead (one register).
+    load_k(my_id);
+    // Small groups keep keys and values of a tile in flight together; large
+    // groups (32+ accumulators) issue the values after the scores so both
+    // tiles are never live at once.
+    constexpr bool kEarlyV = G <= 2;
+    if (kEarlyV) load_v(ids);
+    next_id = tile + 1 < ntiles ? page_id(tile + 1, j_me) : -1;
+
+    // ---- scores, one token per lane
+    float sc[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) sc[h] = 0.f;
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) {
+      const uint4 kv = kreg[c];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const u32x4 qw = q_const[h * NKC + c];  // wave-uniform: scalar loads
+        const uint4 qv = make_uint4(qw.x, qw.y, qw.z, qw.w);
+        if (sizeof(T) == 2) {
+          sc[h] = pa::dot2_bf16(qv.x, kv.x, sc[h]);
+          sc[h] = pa::dot2_bf16(qv.y, kv.y, sc[h]);
+          sc[h] = pa::dot2_bf16(qv.z, kv.z, sc[h]);
+          sc[h] = pa::dot2_bf16(qv.w, kv.w, sc[h]);
+        } else {
+          sc[h] = fmaf(__uint_as_float(qv.x), __uint_as_float(kv.x), sc[h]);
+          sc[h] = fmaf(__uint_as_float(qv.y), __uint_as_float(kv.y), sc[h]);
+          sc[h] = fmaf(__uint_as_float(qv.z), __uint_as_float(kv.z), sc[h]);
+          sc[h] = fmaf(__uint_as_float(qv.w), __uint_as_float(kv.w), sc[h]);
+        }
+      }
+    }
+    if (!kEarlyV) load_v(ids);
+
+    const bool tok_ok = tile_start + lane < part_end;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float sv = tok_ok ? sc[h] * scale_log2 : -INFINITY;
+      const float m_new = fmaxf(m[h], pa::wave_max(sv));
+      const float alpha = pa::fast_exp2(m[h] - m_new);
+      const float p = pa::fast_exp2(sv - m_new);
+      l[h] = l[h] * alpha + p;
+#pragma unroll
+      for (int k = 0; k < NVI; ++k) acc[h][k] *= alpha;
+      m[h] = m_new;
+      if (PVB)
+        p_lds[h * kTile + lane] = static_cast<p_t>(pa::f32_to_bf16_bits(p));
+      else
+        p_lds[h * kTile + lane] = static_cast<p_t>(p);
+    }
+    __syncthreads();
+
+    // ---- weighted values
+    if (tile_start + kTile > part_end) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int keep = part_end - (tile_start + 16 * j + vtok);
+        if (keep < X) {
+#pragma unroll
+          for (int k = 0; k < NVI; ++k) vreg[j][k] = mask_chunk<T>(vreg[j][k], keep);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (ids[j] < 0) continue;
+      int pofs = 16 * j + vtok;
+      if (G > 2) asm volatile("" : "+v"(pofs));  // weights of one page at a time
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const p_t* pp = p_lds + h * kTile + pofs;
+        if (PVB) {
+          const uint4 pw = ld16(pp);
+#pragma unroll
+          for (int k = 0; k < NVI; ++k) {
+            float a = acc[h][k];
+            a = pa::dot2_bf16(pw.x, vreg[j][k].x, a);
+            a = pa::dot2_bf16(pw.y, vreg[j][k].y, a);
+            a = pa::dot2_bf16(pw.z, vreg[j][k].z, a);
+            a = pa::dot2_bf16(pw.w, vreg[j][k].w, a);
+            acc[h][k] = a;
+          }
+        } else if (sizeof(T) == 2) {
+          const uint4 p0 = ld16(pp);
+          const uint4 p1 = ld16(pp + 4);
+          const float pf[8] = {__uint_as_float(p0.x), __uint_as_float(p0.y),
+                               __uint_as_float(p0.z), __uint_as_float(p0.w),
+                               __uint_as_float(p1.x), __uint_as_float(p1.y),
+                               __uint_as_float(p1.z), __uint_as_float(p1.w)};
+#pragma unroll
+          for (int k = 0; k < NVI; ++k) {
+            const uint32_t w[4] = {vreg[j][k].x, vreg[j][k].y, vreg[j][k].z, vreg[j][k].w};
+            float a = acc[h][k];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              a = fmaf(pf[2 * i], pa::bf16_lo(w[i]), a);
+              a = fmaf(pf[2 * i + 1], pa::bf16_hi(w[i]), a);
+            }
+            acc[h][k] = a;
+          }
+        } else {
+          const uint4 p0 = ld16(pp);
+#pragma unroll
+          for (int k = 0; k < NVI; ++k) {
+            float a = acc[h][k];
+            a = fmaf(__uint_as_float(p0.x), __uint_as_float(vreg[j][k].x), a);
+            a = fmaf(__uint_as_float(p0.y), __uint_as_float(vreg[j][k].y), a);
+            a = fmaf(__uint_as_float(p0.z), __uint_as_float(vreg[j][k].z), a);
+            a = fmaf(__uint_as_float(p0.w), __uint_as_float(vreg[j][k].w), a);
+            acc[h][k] = a;
+          }
+        }
+      }
+    }
+    __syncthreads();  // p_lds is rewritten by the next tile
+  }
+
+  // ---- combine lanes and write
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float lt = pa::wave_sum(l[h]);
+    const float inv = 1.f / lt;
+#pragma unroll
+    for (int k = 0; k < NVI; ++k) {
+      float a = acc[h][k];
+#pragma unroll
+      for (int msk = 1; msk < LPR; msk <<= 1) a += __shfl_xor(a, msk, 64);
+      const int d = k * DPI + vrow;
+      if (lane % LPR == 0) {
+        if (nparts_s == 1) {
+          store_out<T>(out + out_row + h * D + d, a * inv);
+        } else {
+          const int64_t row = (static_cast<int64_t>(s) * num_heads + h0 + h) * num_parts + part;
+          ws_o[row * D + d] = a * inv;
+        }
+      }
+    }
+    if (nparts_s > 1 && lane == 0) {
+      const int64_t row = (static_cast<int64_t>(s) * num_heads + h0 + h) * num_parts + part;
+      ws_ml[2 * row] = m[h];
+      ws_ml[2 * row + 1] = lt;
+    }
+  }
+}
+
+// One wave per (head, sequence): merge the partitions of sequences that have
+// more than one.  out = sum_p w_p o_p / sum_p w_p, w_p = l_p * 2^(m_p - M).
+template <typename T, int D>
+__global__ __launch_bounds__(64) void decode_merge_kernel(
+    T* __restrict__ out, const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
+    const int32_t* __restrict__ context_lens, int32_t num_heads, int32_t num_parts,
+    int32_t partition) {
+  const int lane = threadIdx.x;
+  const int h = blockIdx.x;
+  const int s = blockIdx.y;
+  const int L = context_lens[s];
+  const int n = (L + partition - 1) / partition;
+  if (n <= 1) return;
+  const int64_t row0 = (static_cast<int64_t>(s) * num_heads + h) * num_parts;
+  float M = -INFINITY;
+  for (int p = 0; p < n; ++p) M = fmaxf(M, ws_ml[2 * (row0 + p)]);
+  constexpr int PER = D / 64;
+  float o[PER] = {};
+  float wsum = 0.f;
+  for (int p = 0; p < n; ++p) {
+    const float w = ws_ml[2 * (row0 + p) + 1] * pa::fast_exp2(ws_ml[2 * (row0 + p)] - M);
+    wsum += w;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) o[i] = fmaf(w, ws_o[(row0 + p) * D + i * 64 + lane], o[i]);
+  }
+  const float inv = 1.f / wsum;
+  T* dst = out + (static_cast<int64_t>(s) * num_heads + h) * D;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) store_out<T>(dst + i * 64 + lane, o[i] * inv);
+}
+
+constexpr size_t kAlign = 256;
+
+size_t ws_bytes(int64_t B, int64_t H, int64_t D, int64_t parts) {
+  if (parts <= 1) return 0;
+  const size_t o = static_cast<size_t>(B * H * parts * D) * sizeof(float);
+  const size_t ml = static_cast<size_t>(B * H * parts * 2) * sizeof(float);
+  return ((o + kAlign - 1) / kAlign) * kAlign + ml + kAlign;
+}
+
+template <typename T, int D, int G, bool PVB>
+int launch_decode(void* out, const void* q, const void* kc, const void* vc, const int32_t* bt,
+                  int32_t max_blocks, const int32_t* lens, int32_t B, int32_t H, int32_t KVH,
+                  int32_t parts, int32_t partition, float scale_log2, void* ws, hipStream_t st) {
+  float* ws_o = nullptr;
+  float* ws_ml = nullptr;
+  if (parts > 1) {
+    uintptr_t base = (reinterpret_cast<uintptr_t>(ws) + kAlign - 1) & ~(kAlign - 1);
+    ws_o = reinterpret_cast<float*>(base);
+    const size_t o = static_cast<size_t>(B) * H * parts * D * sizeof(float);
+    ws_ml = reinterpret_cast<float*>(base + ((o + kAlign - 1) / kAlign) * kAlign);
+  }
+  hipLaunchKernelGGL((decode_partition_kernel<T, D, G, PVB>), dim3(parts, KVH, B), dim3(64), 0, st,
+                     static_cast<T*>(out), ws_o, ws_ml, static_cast<const T*>(q),
+                     static_cast<const T*>(kc), static_cast<const T*>(vc), bt, max_blocks, lens, H,
+                     KVH, parts, partition, scale_log2);
+  if (parts > 1)
+    hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(H, B), dim3(64), 0, st,
+                       static_cast<T*>(out), ws_o, ws_ml, lens, H, parts, partition);
+  return pa_launch_status();
+}
+
+template <typename T, int D>
+int dispatch_group(int G, void* out, const void* q, const void* kc, const void* vc,
+                   const int32_t* bt, int32_t mb, const int32_t* lens, int32_t B, int32_t H,
+                   int32_t KVH, int32_t parts, int32_t partition, float sl2, void* ws,
+                   hipStream_t st) {
+  constexpr bool kBf = sizeof(T) == 2;
+  switch (G) {
+    case 1: return launch_decode<T, D, 1, false>(out, q, kc, vc, bt, mb, lens, B, H, KVH, parts, partition, sl2, ws, st);
+    case 2: return launch_decode<T, D, 2, false>(out, q, kc, vc, bt, mb, lens, B, H, KVH, parts, partition, sl2, ws, st);
+    case 4: return launch_decode<T, D, 4, kBf>(out, q, kc, vc, bt, mb, lens, B, H, KVH, parts, partition, sl2, ws, st);
+    case 8: return launch_decode<T, D, 8, kBf>(out, q, kc, vc, bt, mb, lens, B, H, KVH, parts, partition, sl2, ws, st);
+    default: return PA_ERR_UNSUPPORTED;
+  }
+}
+
+int64_t parts_for(int32_t max_context_len, int32_t partition) {
+  if (partition <= 0) return 1;
+  return max_context_len <= 0 ? 1 : (static_cast<int64_t>(max_context_len) + partition - 1) / partition;
+}
+
+}  // namespace
+
+extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                            int32_t max_context_len, int32_t partition) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0) return 0;
+  return ws_bytes(num_seqs, num_heads, head_dim, parts_for(max_context_len, partition));
+}
+
+extern "C" int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int32_t num_blocks, float scale, int32_t partition,
+                         int32_t max_context_len, void* workspace, size_t workspace_bytes,
+                         int32_t dtype, void* stream) {
+  if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
+      num_blocks <= 0 || partition < 0 || max_context_len < 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (block_size != kBS || (head_dim != 64 && head_dim != 128)) return PA_ERR_UNSUPPORTED;
+  if (partition % kTile != 0) return PA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * kBS)
+    return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return PA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
+       reinterpret_cast<uintptr_t>(v_cache)) & 15)
+    return PA_ERR_INVALID_ARG;
+  if (num_seqs > 65535 || num_kv_heads > 65535) return PA_ERR_INVALID_ARG;
+  // One pass when unpartitioned: a single "partition" covering the longest
+  // context, rounded up to whole tiles.
+  int32_t part = partition;
+  if (part == 0) part = static_cast<int32_t>(((std::max(max_context_len, 1) + kTile - 1) / kTile) * kTile);
+  const int64_t parts = parts_for(max_context_len, part);
+  if (parts > 0x7fffffff) return PA_ERR_INVALID_ARG;
+  const size_t need = ws_bytes(num_seqs, num_heads, head_dim, parts);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+  const int G = num_heads / num_kv_heads;
+  const float sl2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int32_t P = static_cast<int32_t>(parts);
+  if (dtype == PA_BF16) {
+    if (head_dim == 128)
+      return dispatch_group<uint16_t, 128>(G, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads, num_kv_heads, P, part, sl2, workspace, st);
+    return dispatch_group<uint16_t, 64>(G, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads, num_kv_heads, P, part, sl2, workspace, st);
+  }
+  if (head_dim == 128)
+    return dispatch_group<float, 128>(G, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads, num_kv_heads, P, part, sl2, workspace, st);
+  return dispatch_group<float, 64>(G, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads, num_kv_heads, P, part, sl2, workspace, st);
+}

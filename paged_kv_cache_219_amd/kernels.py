@@ -1,0 +1,168 @@
+"""Torch-facing binding of libpa's kernel entry points.
+
+Same names as the C ABI.  Each function validates shapes/dtypes on the host,
+then passes raw device pointers and the current HIP stream to libpa.  Torch
+only provides device memory and the stream; all work runs in libpa's HIP
+kernels.  ``check_device_args=True`` additionally copies block tables and
+context lengths to the host and verifies the preconditions libpa does not
+check on the device (useful in tests; it synchronises).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from ._lib import PA_BF16, PA_F32, check, lib
+
+BLOCK_SIZE = 16
+_DT = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
+
+
+def chunk_elems(dtype: torch.dtype) -> int:
+    """X: elements per 16-byte chunk of the key layout."""
+    return 16 // torch.tensor([], dtype=dtype).element_size()
+
+
+def new_kv_cache(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype,
+                 device="cuda", block_size: int = BLOCK_SIZE):
+    """Uninitialised (k_cache, v_cache) in libpa's layout:
+    k_cache [num_blocks, num_kv_heads, head_dim // X, block_size, X],
+    v_cache [num_blocks, num_kv_heads, head_dim, block_size]."""
+    x = chunk_elems(dtype)
+    k = torch.empty((num_blocks, num_kv_heads, head_dim // x, block_size, x), dtype=dtype, device=device)
+    v = torch.empty((num_blocks, num_kv_heads, head_dim, block_size), dtype=dtype, device=device)
+    return k, v
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _cache_dims(k_cache: torch.Tensor, v_cache: torch.Tensor):
+    if k_cache.dim() != 5 or v_cache.dim() != 4:
+        raise ValueError("k_cache must be 5-D and v_cache 4-D (libpa layout)")
+    nb, kvh, dx, bs, x = k_cache.shape
+    d = dx * x
+    if tuple(v_cache.shape) != (nb, kvh, d, bs):
+        raise ValueError(f"v_cache shape {tuple(v_cache.shape)} does not match k_cache {tuple(k_cache.shape)}")
+    if x != chunk_elems(k_cache.dtype) or v_cache.dtype != k_cache.dtype:
+        raise ValueError("cache dtype/chunk mismatch")
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("caches must be contiguous")
+    return nb, kvh, d, bs
+
+
+def _check_tables(block_tables, context_lens, num_blocks, block_size):
+    bt = block_tables.cpu().numpy()
+    lens = context_lens.cpu().numpy()
+    mb = bt.shape[1]
+    for s, L in enumerate(lens):
+        if L < 0 or L > mb * block_size:
+            raise ValueError(f"context_lens[{s}]={L} outside [0, {mb * block_size}]")
+        used = bt[s, : -(-int(L) // block_size)]
+        if used.size and (used.min() < 0 or used.max() >= num_blocks):
+            raise ValueError(f"block_tables[{s}] names a block outside the pool")
+
+
+def pa_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, check_device_args=False):
+    nb, kvh, d, bs = _cache_dims(k_cache, v_cache)
+    T = key.shape[0]
+    if key.shape[1:] != (kvh, d) or value.shape[1:] != (kvh, d) or value.shape[0] != T:
+        raise ValueError("key/value must be [T, num_kv_heads, head_dim]")
+    if key.dtype != k_cache.dtype or value.dtype != k_cache.dtype:
+        raise TypeError("key/value dtype must match the cache")
+    if key.stride(2) != 1 or key.stride(1) != d or value.stride(2) != 1 or value.stride(1) != d:
+        raise ValueError("key/value heads must be contiguous rows")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,) or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be contiguous int64 [T]")
+    if check_device_args and T:
+        s = slot_mapping.cpu().numpy()
+        s = s[s >= 0]
+        if s.size and (s.max() >= nb * bs or len(np.unique(s)) != s.size):
+            raise ValueError("slots out of range or repeated")
+    check("pa_reshape_and_cache", lib().pa_reshape_and_cache(
+        key.data_ptr(), value.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        slot_mapping.data_ptr(), T, key.stride(0), value.stride(0), kvh, d, bs, nb,
+        _dtype(k_cache), _stream(k_cache)))
+
+
+def pa_copy_blocks(k_cache, v_cache, pairs):
+    nb, kvh, d, bs = _cache_dims(k_cache, v_cache)
+    if pairs.dtype != torch.int32 or pairs.dim() != 2 or pairs.shape[1] != 2 or not pairs.is_contiguous():
+        raise ValueError("pairs must be contiguous int32 [n, 2]")
+    check("pa_copy_blocks", lib().pa_copy_blocks(
+        k_cache.data_ptr(), v_cache.data_ptr(), pairs.data_ptr(), pairs.shape[0], kvh, d, bs, nb,
+        _dtype(k_cache), _stream(k_cache)))
+
+
+def pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, partition) -> int:
+    return int(lib().pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len,
+                                               partition))
+
+
+def decode_workspace(num_seqs, num_heads, head_dim, max_context_len, partition, device="cuda"):
+    n = pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, partition)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float, partition: int,
+              max_context_len: int, workspace=None, check_device_args=False):
+    nb, kvh, d, bs = _cache_dims(k_cache, v_cache)
+    B, H = q.shape[0], q.shape[1]
+    if q.shape != (B, H, d) or out.shape != q.shape or not (q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("q/out must be contiguous [B, H, head_dim]")
+    if q.dtype != k_cache.dtype or out.dtype != q.dtype:
+        raise TypeError("q/out dtype must match the cache")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B \
+            or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be contiguous int32 [B, max_blocks]")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (B,):
+        raise ValueError("context_lens must be int32 [B]")
+    if check_device_args:
+        _check_tables(block_tables, context_lens, nb, bs)
+        if int(context_lens.max()) > max_context_len:
+            raise ValueError("max_context_len below a context length")
+    need = pa_decode_workspace_bytes(B, H, d, max_context_len, partition)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    check("pa_decode", lib().pa_decode(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(), B, H, kvh, d, bs,
+        nb, float(scale), int(partition), int(max_context_len), wptr, wbytes, _dtype(q),
+        _stream(q)))
+
+
+def pa_prefill_chunk(out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens,
+                     max_query_len: int, scale: float, check_device_args=False):
+    nb, kvh, d, bs = _cache_dims(k_cache, v_cache)
+    T, H = q.shape[0], q.shape[1]
+    B = context_lens.shape[0]
+    if q.shape != (T, H, d) or out.shape != q.shape or not (q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("q/out must be contiguous [T, H, head_dim]")
+    if q.dtype != k_cache.dtype or out.dtype != q.dtype:
+        raise TypeError("q/out dtype must match the cache")
+    if query_start_loc.dtype != torch.int32 or query_start_loc.shape != (B + 1,):
+        raise ValueError("query_start_loc must be int32 [B+1]")
+    if block_tables.dtype != torch.int32 or block_tables.shape[0] != B or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be contiguous int32 [B, max_blocks]")
+    if check_device_args:
+        _check_tables(block_tables, context_lens, nb, bs)
+        qsl = query_start_loc.cpu().numpy()
+        lens = context_lens.cpu().numpy()
+        nq = np.diff(qsl)
+        if qsl[0] != 0 or qsl[-1] != T or (nq < 0).any() or (nq > max_query_len).any() or (nq > lens).any():
+            raise ValueError("query_start_loc inconsistent with q / context_lens")
+    check("pa_prefill_chunk", lib().pa_prefill_chunk(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_tables.data_ptr(), block_tables.shape[1], query_start_loc.data_ptr(),
+        context_lens.data_ptr(), B, int(max_query_len), H, kvh, d, bs, nb, float(scale),
+        _dtype(q), _stream(q)))

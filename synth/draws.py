@@ -10,6 +10,8 @@ Stream numbering (per seed):
   1            the physical-block placement permutation (``free_order``)
   100 + j      K and V of the tokens appended by the j-th ``append`` op
   10**6 + k    the queries of batch step k
+  2*10**6 + k  K and V of the tokens appended by extra decode step k >= 1
+               (benchmarks that decode several steps in a row)
 
 Values are N(0, 1) drawn in float32 (numpy's float32 normal sampler).  bf16
 workloads store them rounded to bfloat16 with round-to-nearest-even, kept as
@@ -28,6 +30,7 @@ STREAM_STRUCTURE = 0
 STREAM_PLACEMENT = 1
 STREAM_APPEND0 = 100
 STREAM_QUERY0 = 10**6
+STREAM_EXTRA_STEP0 = 2 * 10**6
 
 
 def rng(seed: int, stream: int) -> np.random.Generator:
@@ -111,6 +114,13 @@ class Script:
         """(key, value) of an append op: arrays [n, num_kv_heads, head_dim]."""
         s = self.spec
         return kv_tokens(self.seed, op.stream, op.n, s.num_kv_heads, s.head_dim, s.dtype)
+
+    def step_kv(self, step: int):
+        """(key, value) [len(batch), KVH, D] of one more decode token per
+        sequence, for decode step ``step`` >= 1 after the script's own step."""
+        s = self.spec
+        return kv_tokens(self.seed, STREAM_EXTRA_STEP0 + step, len(self.batch), s.num_kv_heads,
+                         s.head_dim, s.dtype)
 
     def q(self, step: int = 0):
         """Queries of the batch step: [sum(query_lens), num_heads, head_dim]."""
