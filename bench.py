@@ -110,6 +110,7 @@ def bench_decode(name: str, steps: int, warmup: int):
     kv_total = 0
     uniq_total = 0
     ncow_total = 0
+    snap = []
     torch.cuda.synchronize()
     for i in range(total):
         if i == warmup:
@@ -139,11 +140,13 @@ def bench_decode(name: str, steps: int, warmup: int):
             dec_ev[i - warmup][1].record(stream)
             kv_total += kv_bytes(lens, spec)
             if name.startswith("shared_prefix"):
-                uniq_total += unique_kv_bytes(tables, lens, spec)
+                snap.append((tables.copy(), lens.copy()))  # accounted after timing
             ncow_total += len(cow)
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    for tables, lens in snap:
+        uniq_total += unique_kv_bytes(tables, lens, spec)
     step_ms = t0.elapsed_time(t1) / steps
     dec_ms = float(np.mean([a.elapsed_time(b) for a, b in dec_ev]))
     kv_step = kv_total / steps
