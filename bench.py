@@ -87,7 +87,8 @@ def bench_decode(name: str, steps: int, warmup: int):
     mb = sc.max_blocks_per_seq
     lens0 = np.array(sc.notes["context_lens"])
     max_ctx = int(lens0.max()) + total
-    ws = decode_workspace(B, spec.num_heads, spec.head_dim, max_ctx, spec.partition, dev)
+    ws = decode_workspace(B, spec.num_heads, spec.num_kv_heads, spec.head_dim, max_ctx,
+                          spec.partition, dev)
     seqs = np.array(sc.batch, np.int64)
     ones = np.ones(B, np.int32)
     R = 3  # ring of pinned host buffers
@@ -266,6 +267,30 @@ def cpu_baseline(budget_s: float = 12.0):
             "seq_tokens_per_s": n / elapsed}
 
 
+def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
+    """A plain device-to-device copy of ``nbytes`` (torch's copy kernel): its
+    rate is the achievable streaming bandwidth, and under rocprofv3 --pmc its
+    FETCH_SIZE / WRITE_SIZE per dispatch calibrate the counters against a
+    known byte count."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "ms": ms,
+            "copy_GBs": 2 * nbytes / (ms * 1e-3) / 1e9}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -274,6 +299,7 @@ def main():
     ap.add_argument("--configs", default="gqa_decode_bf16,shared_prefix_bf16,chunked_prefill_bf16",
                     help="extra workloads reported under 'workloads' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy-calibration", action="store_true")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {a.gpus}): this build has no multi-GPU path.",
@@ -295,6 +321,10 @@ def main():
             print(f"[bench] {name}: decode {r['decode_ms']:.3f} ms = {r['decode_kv_GBs']:.0f} GB/s",
                   file=sys.stderr, flush=True)
         extras.append(r)
+    copy = None if a.no_copy_calibration else copy_calibration()
+    if copy:
+        print(f"[bench] plain copy: {copy['copy_GBs']:.0f} GB/s (read+write)", file=sys.stderr,
+              flush=True)
     cpu = None
     if not a.no_cpu_baseline:
         cpu = cpu_baseline()
@@ -323,6 +353,7 @@ def main():
                      "algorithmic_bytes_per_launch": head["kv_bytes_per_step"],
                      "launch_ms": head["decode_ms"]},
         "cpu_baseline": cpu,
+        "copy_calibration": copy,
         "workloads": [head] + extras,
     }
     print(json.dumps(line), flush=True)

@@ -39,6 +39,7 @@ namespace {
 
 constexpr int kBS = 16;
 constexpr int kTile = 64;
+constexpr uint32_t kXcds = 8;  // MI355X: 8 XCDs, workgroups dispatched round-robin
 
 template <typename T, int D>
 struct Geo {
@@ -80,23 +81,42 @@ __device__ __forceinline__ uint4 mask_chunk(uint4 v, int keep) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// Scratch layout (device workspace): one uint32 arrival counter per (seq, kv
+// head), then per (seq, head, partition) the normalised partial output [D]
+// and the pair (m, l).
+struct Partials {
+  uint32_t* counters;
+  float* o;
+  float* ml;
+};
+
 template <typename T, int D, int G, bool PVB>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_partition_kernel(
-    T* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
-    const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
-    const int32_t* __restrict__ block_tables, int32_t max_blocks,
-    const int32_t* __restrict__ context_lens, int32_t num_heads, int32_t num_kv_heads,
-    int32_t num_parts, int32_t partition, float scale_log2) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(
+    T* __restrict__ out, Partials ws, const T* __restrict__ q, const T* __restrict__ kc,
+    const T* __restrict__ vc, const int32_t* __restrict__ block_tables, int32_t max_blocks,
+    const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t num_parts, int32_t partition, float scale_log2) {
   using Gm = Geo<T, D>;
   constexpr int X = Gm::X, NKC = Gm::NKC, LPR = Gm::LPR, DPI = Gm::DPI, NVI = Gm::NVI;
   typedef typename std::conditional<PVB, uint16_t, float>::type p_t;
 
   __shared__ __attribute__((aligned(16))) p_t p_lds[G * kTile];
 
+  // Workgroups are handed to the 8 XCDs round-robin (WG i -> XCD i % 8).
+  // Give XCD x the x-th contiguous slice of the logical order (kv head,
+  // partition, sequence), sequence fastest: every XCD gets whole kv heads
+  // (equal work), a sequence's partitions stay on one XCD, and sequences
+  // adjacent in the batch -- e.g. samples sharing a prompt's blocks -- read
+  // the same pages back to back through that XCD's L2.
+  const uint32_t per_xcd = gridDim.x / kXcds;
+  const uint32_t li = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  const int s = static_cast<int>(li % static_cast<uint32_t>(num_seqs));
+  const uint32_t gp = li / static_cast<uint32_t>(num_seqs);
+  const int part = static_cast<int>(gp % static_cast<uint32_t>(num_parts));
+  const int g = static_cast<int>(gp / static_cast<uint32_t>(num_parts));
+  if (g >= num_kv_heads) return;  // grid padding
+
   const int lane = threadIdx.x;
-  const int part = blockIdx.x;
-  const int g = blockIdx.y;
-  const int s = blockIdx.z;
   const int h0 = g * G;
   const int L = context_lens[s];
   const int part_start = part * partition;
@@ -301,11 +321,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     __syncthreads();  // p_lds is rewritten by the next tile
   }
 
-  // ---- combine lanes and write
+  // ---- combine lanes; write the output, or this partition's partial
+  float lt[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float lt = pa::wave_sum(l[h]);
-    const float inv = 1.f / lt;
+    lt[h] = pa::wave_sum(l[h]);
+    const float inv = 1.f / lt[h];
 #pragma unroll
     for (int k = 0; k < NVI; ++k) {
       float a = acc[h][k];
@@ -317,77 +338,84 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
           store_out<T>(out + out_row + h * D + d, a * inv);
         } else {
           const int64_t row = (static_cast<int64_t>(s) * num_heads + h0 + h) * num_parts + part;
-          ws_o[row * D + d] = a * inv;
+          ws.o[row * D + d] = a * inv;
         }
       }
     }
-    if (nparts_s > 1 && lane == 0) {
+  }
+  if (nparts_s == 1) return;
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
       const int64_t row = (static_cast<int64_t>(s) * num_heads + h0 + h) * num_parts + part;
-      ws_ml[2 * row] = m[h];
-      ws_ml[2 * row + 1] = lt;
+      ws.ml[2 * row] = m[h];
+      ws.ml[2 * row + 1] = lt[h];
     }
   }
-}
 
-// One wave per (head, sequence): merge the partitions of sequences that have
-// more than one.  out = sum_p w_p o_p / sum_p w_p, w_p = l_p * 2^(m_p - M).
-template <typename T, int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(
-    T* __restrict__ out, const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
-    const int32_t* __restrict__ context_lens, int32_t num_heads, int32_t num_parts,
-    int32_t partition) {
-  const int lane = threadIdx.x;
-  const int h = blockIdx.x;
-  const int s = blockIdx.y;
-  const int L = context_lens[s];
-  const int n = (L + partition - 1) / partition;
-  if (n <= 1) return;
-  const int64_t row0 = (static_cast<int64_t>(s) * num_heads + h) * num_parts;
-  float M = -INFINITY;
-  for (int p = 0; p < n; ++p) M = fmaxf(M, ws_ml[2 * (row0 + p)]);
+  // ---- the last partition of (s, g) to finish merges all of them, in
+  // partition order (the result does not depend on arrival order):
+  // out = sum_p w_p o_p / sum_p w_p, w_p = l_p * 2^(m_p - max_p m_p).
+  __syncthreads();
+  __threadfence();  // release this wave's partials device-wide (other XCDs)
+  uint32_t* ctr = ws.counters + static_cast<int64_t>(s) * num_kv_heads + g;
+  uint32_t prev = 0;
+  if (lane == 0) prev = atomicAdd(ctr, 1u);
+  prev = __shfl(prev, 0, 64);
+  if (prev != static_cast<uint32_t>(nparts_s - 1)) return;
+  __threadfence();  // acquire: see every other partition's partials
+  if (lane == 0) atomicExch(ctr, 0u);  // leave the counter zero for the next call
   constexpr int PER = D / 64;
-  float o[PER] = {};
-  float wsum = 0.f;
-  for (int p = 0; p < n; ++p) {
-    const float w = ws_ml[2 * (row0 + p) + 1] * pa::fast_exp2(ws_ml[2 * (row0 + p)] - M);
-    wsum += w;
+#pragma unroll 1
+  for (int h = 0; h < G; ++h) {
+    const int64_t row0 = (static_cast<int64_t>(s) * num_heads + h0 + h) * num_parts;
+    float M = -INFINITY;
+    for (int p = 0; p < nparts_s; ++p) M = fmaxf(M, ws.ml[2 * (row0 + p)]);
+    float o[PER] = {};
+    float wsum = 0.f;
+    for (int p = 0; p < nparts_s; ++p) {
+      const float w = ws.ml[2 * (row0 + p) + 1] * pa::fast_exp2(ws.ml[2 * (row0 + p)] - M);
+      wsum += w;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) o[i] = fmaf(w, ws_o[(row0 + p) * D + i * 64 + lane], o[i]);
+      for (int i = 0; i < PER; ++i) o[i] = fmaf(w, ws.o[(row0 + p) * D + i * 64 + lane], o[i]);
+    }
+    const float inv = 1.f / wsum;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) store_out<T>(out + out_row + h * D + i * 64 + lane, o[i] * inv);
   }
-  const float inv = 1.f / wsum;
-  T* dst = out + (static_cast<int64_t>(s) * num_heads + h) * D;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) store_out<T>(dst + i * 64 + lane, o[i] * inv);
 }
 
 constexpr size_t kAlign = 256;
 
-size_t ws_bytes(int64_t B, int64_t H, int64_t D, int64_t parts) {
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// counters | partial outputs | (m, l) pairs, each region 256-byte aligned
+size_t ws_bytes(int64_t B, int64_t KVH, int64_t H, int64_t D, int64_t parts) {
   if (parts <= 1) return 0;
-  const size_t o = static_cast<size_t>(B * H * parts * D) * sizeof(float);
-  const size_t ml = static_cast<size_t>(B * H * parts * 2) * sizeof(float);
-  return ((o + kAlign - 1) / kAlign) * kAlign + ml + kAlign;
+  return align_up(static_cast<size_t>(B * KVH) * sizeof(uint32_t)) +
+         align_up(static_cast<size_t>(B * H * parts * D) * sizeof(float)) +
+         static_cast<size_t>(B * H * parts * 2) * sizeof(float);
 }
 
 template <typename T, int D, int G, bool PVB>
 int launch_decode(void* out, const void* q, const void* kc, const void* vc, const int32_t* bt,
                   int32_t max_blocks, const int32_t* lens, int32_t B, int32_t H, int32_t KVH,
                   int32_t parts, int32_t partition, float scale_log2, void* ws, hipStream_t st) {
-  float* ws_o = nullptr;
-  float* ws_ml = nullptr;
+  Partials p{nullptr, nullptr, nullptr};
   if (parts > 1) {
-    uintptr_t base = (reinterpret_cast<uintptr_t>(ws) + kAlign - 1) & ~(kAlign - 1);
-    ws_o = reinterpret_cast<float*>(base);
-    const size_t o = static_cast<size_t>(B) * H * parts * D * sizeof(float);
-    ws_ml = reinterpret_cast<float*>(base + ((o + kAlign - 1) / kAlign) * kAlign);
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    p.counters = reinterpret_cast<uint32_t*>(base);
+    base += align_up(static_cast<size_t>(B) * KVH * sizeof(uint32_t));
+    p.o = reinterpret_cast<float*>(base);
+    base += align_up(static_cast<size_t>(B) * H * parts * D * sizeof(float));
+    p.ml = reinterpret_cast<float*>(base);
   }
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, G, PVB>), dim3(parts, KVH, B), dim3(64), 0, st,
-                     static_cast<T*>(out), ws_o, ws_ml, static_cast<const T*>(q),
-                     static_cast<const T*>(kc), static_cast<const T*>(vc), bt, max_blocks, lens, H,
-                     KVH, parts, partition, scale_log2);
-  if (parts > 1)
-    hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(H, B), dim3(64), 0, st,
-                       static_cast<T*>(out), ws_o, ws_ml, lens, H, parts, partition);
+  const int64_t items = static_cast<int64_t>(parts) * KVH * B;
+  const int64_t grid = (items + kXcds - 1) / kXcds * kXcds;
+  hipLaunchKernelGGL((decode_kernel<T, D, G, PVB>), dim3(static_cast<uint32_t>(grid)), dim3(64), 0,
+                     st, static_cast<T*>(out), p, static_cast<const T*>(q),
+                     static_cast<const T*>(kc), static_cast<const T*>(vc), bt, max_blocks, lens, B,
+                     H, KVH, parts, partition, scale_log2);
   return pa_launch_status();
 }
 
@@ -413,10 +441,12 @@ int64_t parts_for(int32_t max_context_len, int32_t partition) {
 
 }  // namespace
 
-extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                            int32_t num_kv_heads, int32_t head_dim,
                                             int32_t max_context_len, int32_t partition) {
-  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0) return 0;
-  return ws_bytes(num_seqs, num_heads, head_dim, parts_for(max_context_len, partition));
+  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
+  return ws_bytes(num_seqs, num_kv_heads, num_heads, head_dim,
+                  parts_for(max_context_len, partition));
 }
 
 extern "C" int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -441,14 +471,15 @@ extern "C" int pa_decode(void* out, const void* q, const void* k_cache, const vo
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
        reinterpret_cast<uintptr_t>(v_cache)) & 15)
     return PA_ERR_INVALID_ARG;
-  if (num_seqs > 65535 || num_kv_heads > 65535) return PA_ERR_INVALID_ARG;
   // One pass when unpartitioned: a single "partition" covering the longest
   // context, rounded up to whole tiles.
   int32_t part = partition;
   if (part == 0) part = static_cast<int32_t>(((std::max(max_context_len, 1) + kTile - 1) / kTile) * kTile);
   const int64_t parts = parts_for(max_context_len, part);
   if (parts > 0x7fffffff) return PA_ERR_INVALID_ARG;
-  const size_t need = ws_bytes(num_seqs, num_heads, head_dim, parts);
+  const size_t need = ws_bytes(num_seqs, num_kv_heads, num_heads, head_dim, parts);
+  if (static_cast<int64_t>(parts) * num_kv_heads * num_seqs + kXcds > 0x7fffffffLL)
+    return PA_ERR_INVALID_ARG;
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_ERR_WORKSPACE;
   const int G = num_heads / num_kv_heads;
   const float sl2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
