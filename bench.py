@@ -87,8 +87,7 @@ def bench_decode(name: str, steps: int, warmup: int):
     mb = sc.max_blocks_per_seq
     lens0 = np.array(sc.notes["context_lens"])
     max_ctx = int(lens0.max()) + total
-    ws = decode_workspace(B, spec.num_heads, spec.num_kv_heads, spec.head_dim, max_ctx,
-                          spec.partition, dev)
+    ws = decode_workspace(B, spec.num_heads, spec.head_dim, max_ctx, spec.partition, dev)
     seqs = np.array(sc.batch, np.int64)
     ones = np.ones(B, np.int32)
     R = 3  # ring of pinned host buffers

@@ -113,13 +113,12 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t n
 
 /*
  * pa_decode_workspace_bytes -- bytes of device workspace pa_decode needs.
- * Zero when no sequence can span more than one partition.  Layout: one uint32
- * arrival counter per (sequence, kv head), then fp32 partials -- num_seqs *
- * num_heads * ceil(max_context_len / partition) * (head_dim + 2) values --
- * each region 256-byte aligned.
+ * Zero when no sequence can span more than one partition.  Partials are fp32:
+ * num_seqs * num_heads * ceil(max_context_len / partition) * (head_dim + 2)
+ * values, plus alignment.
  */
-size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                                 int32_t head_dim, int32_t max_context_len, int32_t partition);
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition);
 
 /*
  * pa_decode -- one query token per sequence against its paged context.
@@ -141,15 +140,12 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
  *                  The result does not depend on the partition size beyond
  *                  fp32 rounding.  A sequence longer than one partition is
  *                  processed by ceil(L/partition) independent workgroups
- *                  whose partial (max, sum, output) triples are merged with
- *                  log-sum-exp weights by the last of them to finish (one
- *                  kernel launch in all cases).
+ *                  whose partial (max, sum, output) triples a second kernel
+ *                  merges with log-sum-exp weights.
  *   max_context_len  host upper bound of context_lens (sizes the grid).
  *   workspace      device scratch of at least pa_decode_workspace_bytes(...)
- *                  bytes (may be NULL when that is 0).  Its counter region
- *                  (the first num_seqs * num_kv_heads uint32) must be zero
- *                  before the first call that uses the workspace; every call
- *                  leaves it zero again.  The rest is overwritten.  Calls that
+ *                  bytes (may be NULL when that is 0); contents on entry are
+ *                  ignored, contents on exit are unspecified.  Calls that
  *                  overlap in time must not share a workspace.
  * Deterministic: the merge runs in partition order and the reduction order
  * depends only on logical positions, so results do not depend on block

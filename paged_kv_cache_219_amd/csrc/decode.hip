@@ -81,11 +81,10 @@ __device__ __forceinline__ uint4 mask_chunk(uint4 v, int keep) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// Scratch layout (device workspace): one uint32 arrival counter per (seq, kv
-// head), then per (seq, head, partition) the normalised partial output [D]
-// and the pair (m, l).
+// Scratch layout (device workspace): per (seq, head, partition) the
+// normalised partial output [D], then per (seq, head, partition) the pair
+// (m, l).
 struct Partials {
-  uint32_t* counters;
   float* o;
   float* ml;
 };
@@ -175,11 +174,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
       for (int c = 0; c < NKC; ++c) kreg[c] = make_uint4(0, 0, 0, 0);
     }
   };
-  auto load_v = [&](const int (&ids)[4]) {
-    int vofs = lane * X;
-    // pins the value loads here: the scheduler may not lift them above the
-    // score loop (whose chunk barriers are also volatile)
-    if (G > 2) asm volatile("" : "+v"(vofs));
+  auto load_v = [&](const int (&ids)[4], int vofs) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (ids[j] >= 0) {
@@ -209,7 +204,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     // groups (32+ accumulators) issue the values after the scores so both
     // tiles are never live at once.
     constexpr bool kEarlyV = G <= 2;
-    if (kEarlyV) load_v(ids);
+    if (kEarlyV) load_v(ids, lane * X);
     next_id = tile + 1 < ntiles ? page_id(tile + 1, j_me) : -1;
 
     // ---- scores, one token per lane
@@ -236,13 +231,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
         }
       }
     }
-    if (!kEarlyV) load_v(ids);
+    if (!kEarlyV) {
+      // the offset "depends" on the last score, so the scheduler cannot lift
+      // the value loads above the score loop (keys and values never both live)
+      int vofs = lane * X;
+      asm volatile("" : "+v"(vofs) : "v"(sc[G - 1]));
+      load_v(ids, vofs);
+    }
 
     const bool tok_ok = tile_start + lane < part_end;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float sv = tok_ok ? sc[h] * scale_log2 : -INFINITY;
-      const float m_new = fmaxf(m[h], pa::wave_max(sv));
+      const float m_new = fmaxf(m[h], pa::wave_max_u(sv));
       const float alpha = pa::fast_exp2(m[h] - m_new);
       const float p = pa::fast_exp2(sv - m_new);
       l[h] = l[h] * alpha + p;
@@ -325,13 +326,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   float lt[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    lt[h] = pa::wave_sum(l[h]);
+    lt[h] = pa::wave_sum_u(l[h]);
     const float inv = 1.f / lt[h];
 #pragma unroll
     for (int k = 0; k < NVI; ++k) {
       float a = acc[h][k];
-#pragma unroll
-      for (int msk = 1; msk < LPR; msk <<= 1) a += __shfl_xor(a, msk, 64);
+      a += pa::dpp<pa::kDppXor1>(a);  // lanes sharing a value row: xor 1 (and 2)
+      if (LPR == 4) a += pa::dpp<pa::kDppXor2>(a);
       const int d = k * DPI + vrow;
       if (lane % LPR == 0) {
         if (nparts_s == 1) {
@@ -343,8 +344,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
       }
     }
   }
-  if (nparts_s == 1) return;
-  if (lane == 0) {
+  if (nparts_s > 1 && lane == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const int64_t row = (static_cast<int64_t>(s) * num_heads + h0 + h) * num_parts + part;
@@ -352,36 +352,41 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
       ws.ml[2 * row + 1] = lt[h];
     }
   }
+}
 
-  // ---- the last partition of (s, g) to finish merges all of them, in
-  // partition order (the result does not depend on arrival order):
-  // out = sum_p w_p o_p / sum_p w_p, w_p = l_p * 2^(m_p - max_p m_p).
-  __syncthreads();
-  __threadfence();  // release this wave's partials device-wide (other XCDs)
-  uint32_t* ctr = ws.counters + static_cast<int64_t>(s) * num_kv_heads + g;
-  uint32_t prev = 0;
-  if (lane == 0) prev = atomicAdd(ctr, 1u);
-  prev = __shfl(prev, 0, 64);
-  if (prev != static_cast<uint32_t>(nparts_s - 1)) return;
-  __threadfence();  // acquire: see every other partition's partials
-  if (lane == 0) atomicExch(ctr, 0u);  // leave the counter zero for the next call
+// Second pass, one wave per (kv head, sequence) with more than one partition:
+// for each of the G heads, out = sum_p w_p o_p / sum_p w_p with
+// w_p = l_p * 2^(m_p - max_p m_p), partitions in order (deterministic).
+// (Merging inside the first pass would need an agent-scope release per
+// partition -- an L2 write-back on this chip, far costlier than this launch.)
+template <typename T, int D, int G>
+__global__ __launch_bounds__(64) void decode_merge_kernel(
+    T* __restrict__ out, Partials ws, const int32_t* __restrict__ context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t num_parts, int32_t partition) {
+  const int lane = threadIdx.x;
+  const int s = static_cast<int>(blockIdx.x % static_cast<uint32_t>(num_seqs));
+  const int g = static_cast<int>(blockIdx.x / static_cast<uint32_t>(num_seqs));
+  const int L = context_lens[s];
+  const int n = (L + partition - 1) / partition;
+  if (n <= 1) return;
   constexpr int PER = D / 64;
 #pragma unroll 1
-  for (int h = 0; h < G; ++h) {
-    const int64_t row0 = (static_cast<int64_t>(s) * num_heads + h0 + h) * num_parts;
+  for (int h = g * G; h < (g + 1) * G; ++h) {
+    const int64_t row0 = (static_cast<int64_t>(s) * num_heads + h) * num_parts;
     float M = -INFINITY;
-    for (int p = 0; p < nparts_s; ++p) M = fmaxf(M, ws.ml[2 * (row0 + p)]);
+    for (int p = 0; p < n; ++p) M = fmaxf(M, ws.ml[2 * (row0 + p)]);
     float o[PER] = {};
     float wsum = 0.f;
-    for (int p = 0; p < nparts_s; ++p) {
+    for (int p = 0; p < n; ++p) {
       const float w = ws.ml[2 * (row0 + p) + 1] * pa::fast_exp2(ws.ml[2 * (row0 + p)] - M);
       wsum += w;
 #pragma unroll
       for (int i = 0; i < PER; ++i) o[i] = fmaf(w, ws.o[(row0 + p) * D + i * 64 + lane], o[i]);
     }
     const float inv = 1.f / wsum;
+    T* dst = out + (static_cast<int64_t>(s) * num_heads + h) * D;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) store_out<T>(out + out_row + h * D + i * 64 + lane, o[i] * inv);
+    for (int i = 0; i < PER; ++i) store_out<T>(dst + i * 64 + lane, o[i] * inv);
   }
 }
 
@@ -389,11 +394,10 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// counters | partial outputs | (m, l) pairs, each region 256-byte aligned
-size_t ws_bytes(int64_t B, int64_t KVH, int64_t H, int64_t D, int64_t parts) {
+// partial outputs | (m, l) pairs, each region 256-byte aligned
+size_t ws_bytes(int64_t B, int64_t H, int64_t D, int64_t parts) {
   if (parts <= 1) return 0;
-  return align_up(static_cast<size_t>(B * KVH) * sizeof(uint32_t)) +
-         align_up(static_cast<size_t>(B * H * parts * D) * sizeof(float)) +
+  return align_up(static_cast<size_t>(B * H * parts * D) * sizeof(float)) +
          static_cast<size_t>(B * H * parts * 2) * sizeof(float);
 }
 
@@ -401,11 +405,9 @@ template <typename T, int D, int G, bool PVB>
 int launch_decode(void* out, const void* q, const void* kc, const void* vc, const int32_t* bt,
                   int32_t max_blocks, const int32_t* lens, int32_t B, int32_t H, int32_t KVH,
                   int32_t parts, int32_t partition, float scale_log2, void* ws, hipStream_t st) {
-  Partials p{nullptr, nullptr, nullptr};
+  Partials p{nullptr, nullptr};
   if (parts > 1) {
     uint8_t* base = static_cast<uint8_t*>(ws);
-    p.counters = reinterpret_cast<uint32_t*>(base);
-    base += align_up(static_cast<size_t>(B) * KVH * sizeof(uint32_t));
     p.o = reinterpret_cast<float*>(base);
     base += align_up(static_cast<size_t>(B) * H * parts * D * sizeof(float));
     p.ml = reinterpret_cast<float*>(base);
@@ -416,6 +418,9 @@ int launch_decode(void* out, const void* q, const void* kc, const void* vc, cons
                      st, static_cast<T*>(out), p, static_cast<const T*>(q),
                      static_cast<const T*>(kc), static_cast<const T*>(vc), bt, max_blocks, lens, B,
                      H, KVH, parts, partition, scale_log2);
+  if (parts > 1)
+    hipLaunchKernelGGL((decode_merge_kernel<T, D, G>), dim3(static_cast<uint32_t>(B) * KVH),
+                       dim3(64), 0, st, static_cast<T*>(out), p, lens, B, H, KVH, parts, partition);
   return pa_launch_status();
 }
 
@@ -441,12 +446,10 @@ int64_t parts_for(int32_t max_context_len, int32_t partition) {
 
 }  // namespace
 
-extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads,
-                                            int32_t num_kv_heads, int32_t head_dim,
+extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                             int32_t max_context_len, int32_t partition) {
-  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
-  return ws_bytes(num_seqs, num_kv_heads, num_heads, head_dim,
-                  parts_for(max_context_len, partition));
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0) return 0;
+  return ws_bytes(num_seqs, num_heads, head_dim, parts_for(max_context_len, partition));
 }
 
 extern "C" int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -477,7 +480,7 @@ extern "C" int pa_decode(void* out, const void* q, const void* k_cache, const vo
   if (part == 0) part = static_cast<int32_t>(((std::max(max_context_len, 1) + kTile - 1) / kTile) * kTile);
   const int64_t parts = parts_for(max_context_len, part);
   if (parts > 0x7fffffff) return PA_ERR_INVALID_ARG;
-  const size_t need = ws_bytes(num_seqs, num_kv_heads, num_heads, head_dim, parts);
+  const size_t need = ws_bytes(num_seqs, num_heads, head_dim, parts);
   if (static_cast<int64_t>(parts) * num_kv_heads * num_seqs + kXcds > 0x7fffffffLL)
     return PA_ERR_INVALID_ARG;
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_ERR_WORKSPACE;

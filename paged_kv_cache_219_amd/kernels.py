@@ -102,19 +102,14 @@ def pa_copy_blocks(k_cache, v_cache, pairs):
         _dtype(k_cache), _stream(k_cache)))
 
 
-def pa_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
-                              partition) -> int:
-    return int(lib().pa_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
-                                               max_context_len, partition))
+def pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, partition) -> int:
+    return int(lib().pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len,
+                                               partition))
 
 
-def decode_workspace(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition,
-                     device="cuda"):
-    """A zero-filled workspace for pa_decode (its arrival counters must start
-    at zero; pa_decode leaves them zero)."""
-    n = pa_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
-                                  partition)
-    return torch.zeros(max(n, 1), dtype=torch.uint8, device=device)
+def decode_workspace(num_seqs, num_heads, head_dim, max_context_len, partition, device="cuda"):
+    n = pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, partition)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float, partition: int,
@@ -134,9 +129,9 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float
         _check_tables(block_tables, context_lens, nb, bs)
         if int(context_lens.max()) > max_context_len:
             raise ValueError("max_context_len below a context length")
-    need = pa_decode_workspace_bytes(B, H, kvh, d, max_context_len, partition)
+    need = pa_decode_workspace_bytes(B, H, d, max_context_len, partition)
     if workspace is None and need:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     wptr = workspace.data_ptr() if workspace is not None else None
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     check("pa_decode", lib().pa_decode(

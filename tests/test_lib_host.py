@@ -56,9 +56,9 @@ def test_host_argument_checks_reject_before_launch():
     assert dec(H=8, maxL=8 * 16 + 1) == -1
     assert dec(H=8, D=96) == -5
     assert dec(H=8, BS=32) == -5
-    assert L.pa_decode_workspace_bytes(2, 8, 4, 128, 100, 0) == 0
-    assert L.pa_decode_workspace_bytes(2, 8, 4, 128, 64, 64) == 0
-    assert L.pa_decode_workspace_bytes(2, 8, 4, 128, 100, 64) >= 2 * 4 * 4 + 2 * 8 * 2 * 130 * 4
+    assert L.pa_decode_workspace_bytes(2, 8, 128, 100, 0) == 0
+    assert L.pa_decode_workspace_bytes(2, 8, 128, 64, 64) == 0
+    assert L.pa_decode_workspace_bytes(2, 8, 128, 100, 64) >= 2 * 8 * 2 * 130 * 4
     # prefill: fp32 is not supported (matrix-core path is bf16)
     assert L.pa_prefill_chunk(fake, fake, fake, fake, fake, 8, fake, fake, 2, 16, 8, 8, 128, 16, 64,
                               0.1, PA_F32, None) == -5
