@@ -39,7 +39,14 @@ namespace {
 
 constexpr int kBS = 16;
 constexpr int kTile = 64;
-constexpr uint32_t kXcds = 8;  // MI355X: 8 XCDs, workgroups dispatched round-robin
+
+// Orders this wave's LDS accesses: wait for its outstanding LDS operations.
+// Enough to exchange data between lanes of a single-wave workgroup (a
+// workgroup barrier would also wait for every global load in flight).
+__device__ __forceinline__ void lds_wave_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+}
 
 template <typename T, int D>
 struct Geo {
@@ -101,19 +108,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 
   __shared__ __attribute__((aligned(16))) p_t p_lds[G * kTile];
 
-  // Workgroups are handed to the 8 XCDs round-robin (WG i -> XCD i % 8).
-  // Give XCD x the x-th contiguous slice of the logical order (kv head,
-  // partition, sequence), sequence fastest: every XCD gets whole kv heads
-  // (equal work), a sequence's partitions stay on one XCD, and sequences
-  // adjacent in the batch -- e.g. samples sharing a prompt's blocks -- read
-  // the same pages back to back through that XCD's L2.
-  const uint32_t per_xcd = gridDim.x / kXcds;
-  const uint32_t li = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  const int s = static_cast<int>(li % static_cast<uint32_t>(num_seqs));
-  const uint32_t gp = li / static_cast<uint32_t>(num_seqs);
-  const int part = static_cast<int>(gp % static_cast<uint32_t>(num_parts));
-  const int g = static_cast<int>(gp / static_cast<uint32_t>(num_parts));
-  if (g >= num_kv_heads) return;  // grid padding
+  // Logical order (partition, sequence, kv head), kv head fastest, in plain
+  // dispatch order.  Workgroups go to the 8 XCDs round-robin, so XCD x gets
+  // the kv heads congruent to x (equal work per XCD); every kv head is in
+  // flight at once (their pages sit at different offsets inside a block, which
+  // spreads the reads over all HBM channels); the heavy low partitions run
+  // first and the mostly-empty high ones last; and sequences adjacent in the
+  // batch -- e.g. samples sharing a prompt's blocks -- read the same page on
+  // the same XCD a few workgroups apart, through its L2.
+  const uint32_t li = blockIdx.x;
+  const int g = static_cast<int>(li % static_cast<uint32_t>(num_kv_heads));
+  const uint32_t ps = li / static_cast<uint32_t>(num_kv_heads);
+  const int s = static_cast<int>(ps % static_cast<uint32_t>(num_seqs));
+  const int part = static_cast<int>(ps / static_cast<uint32_t>(num_seqs));
+  if (part >= num_parts) return;
 
   const int lane = threadIdx.x;
   const int h0 = g * G;
@@ -159,14 +167,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const int ntiles = (part_end - part_start + kTile - 1) / kTile;
   const int lb_part = part_start / kBS;
 
-  // Per-lane block id of the lane's own page, and validity of the 4 pages.
+  // Block id of this lane's own page (QK layout) for a tile; -1 past the end.
   auto page_id = [&](int tile, int j) -> int {
     const int lb = lb_part + tile * 4 + j;
     return lb * kBS < part_end ? bt_row[lb] : -1;
   };
-  auto load_k = [&](int phys) {
+  auto load_k = [&](int phys, int kofs) {
     if (phys >= 0) {
-      const T* base = kc + phys * blk_stride + head_off + t_me * X;
+      const T* base = kc + phys * blk_stride + head_off + kofs;
 #pragma unroll
       for (int c = 0; c < NKC; ++c) kreg[c] = ld16(base + c * (kBS * X));
     } else {
@@ -187,25 +195,37 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
       }
     }
   };
+  auto page_ids = [&](int my, int (&ids)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ids[j] = __builtin_amdgcn_readlane(my, 16 * j);
+  };
 
-  int next_id = page_id(0, j_me);
+  // Software pipeline inside the wave: block ids are fetched two tiles ahead;
+  // the keys of tile t+1 are issued into the key registers as soon as the
+  // scores of tile t are done, and the values of tile t+1 into the value
+  // registers as soon as tile t's weighted sum is done, so about one and a
+  // half tiles stay in flight per wave with a single set of load registers.
+  // Small groups issue a tile's values together with its keys; large groups
+  // (32+ accumulators) issue them right after the scores.  Each prefetch's
+  // address takes an empty asm dependency on the value computed just before
+  // it, which keeps the scheduler from hoisting the loads into extra
+  // registers.
+  // Large groups are VALU-heavy and register-bound: for them the next tile's
+  // keys are loaded at the top of its own iteration instead (no prefetch).
+  constexpr bool kEarlyV = G <= 2;
+  constexpr bool kPipe = G <= 2;
+  int id_cur = page_id(0, j_me);
+  int id_next = ntiles > 1 ? page_id(1, j_me) : -1;
+  int ids[4];
+  page_ids(id_cur, ids);
+  load_k(id_cur, t_me * X);
+  if (kEarlyV) load_v(ids, lane * X);
 
   for (int tile = 0; tile < ntiles; ++tile) {
     const int tile_start = part_start + tile * kTile;
-    const int my_id = next_id;
-    int ids[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) ids[j] = __builtin_amdgcn_readlane(my_id, 16 * j);
-    // Issue the whole tile's keys and values at once; other waves on the SIMD
-    // compute while these are in flight.  Only the block ids of the next tile
-    // are fetched ahead (one register).
-    load_k(my_id);
-    // Small groups keep keys and values of a tile in flight together; large
-    // groups (32+ accumulators) issue the values after the scores so both
-    // tiles are never live at once.
-    constexpr bool kEarlyV = G <= 2;
-    if (kEarlyV) load_v(ids, lane * X);
-    next_id = tile + 1 < ntiles ? page_id(tile + 1, j_me) : -1;
+    const bool more = tile + 1 < ntiles;
+    const int id_next2 = tile + 2 < ntiles ? page_id(tile + 2, j_me) : -1;
+    if (!kPipe && tile > 0) load_k(id_cur, t_me * X);
 
     // ---- scores, one token per lane
     float sc[G];
@@ -231,12 +251,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
         }
       }
     }
-    if (!kEarlyV) {
-      // the offset "depends" on the last score, so the scheduler cannot lift
-      // the value loads above the score loop (keys and values never both live)
-      int vofs = lane * X;
-      asm volatile("" : "+v"(vofs) : "v"(sc[G - 1]));
-      load_v(ids, vofs);
+    int ids_next[4];
+    page_ids(id_next, ids_next);
+    {
+      int vofs = lane * X, kofs = t_me * X;
+      asm volatile("" : "+v"(vofs), "+v"(kofs) : "v"(sc[G - 1]));
+      if (!kEarlyV) load_v(ids, vofs);
+      if (kPipe && more) load_k(id_next, kofs);
     }
 
     const bool tok_ok = tile_start + lane < part_end;
@@ -255,7 +276,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
       else
         p_lds[h * kTile + lane] = static_cast<p_t>(p);
     }
-    __syncthreads();
+    // The weights are exchanged between lanes of this (single-wave)
+    // workgroup; its LDS operations complete in order, so waiting for the
+    // writes suffices -- and unlike a workgroup barrier this does not wait
+    // for the prefetches in flight.
+    lds_wave_sync();
 
     // ---- weighted values
     if (tile_start + kTile > part_end) {
@@ -319,7 +344,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
         }
       }
     }
-    __syncthreads();  // p_lds is rewritten by the next tile
+    lds_wave_sync();  // p_lds is rewritten by the next tile
+    if (kEarlyV && more) {
+      int vofs = lane * X;
+      asm volatile("" : "+v"(vofs) : "v"(acc[G - 1][NVI - 1]));
+      load_v(ids_next, vofs);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ids[j] = ids_next[j];
+    id_cur = id_next;
+    id_next = id_next2;
   }
 
   // ---- combine lanes; write the output, or this partition's partial
@@ -412,8 +446,7 @@ int launch_decode(void* out, const void* q, const void* kc, const void* vc, cons
     base += align_up(static_cast<size_t>(B) * H * parts * D * sizeof(float));
     p.ml = reinterpret_cast<float*>(base);
   }
-  const int64_t items = static_cast<int64_t>(parts) * KVH * B;
-  const int64_t grid = (items + kXcds - 1) / kXcds * kXcds;
+  const int64_t grid = static_cast<int64_t>(parts) * KVH * B;
   hipLaunchKernelGGL((decode_kernel<T, D, G, PVB>), dim3(static_cast<uint32_t>(grid)), dim3(64), 0,
                      st, static_cast<T*>(out), p, static_cast<const T*>(q),
                      static_cast<const T*>(kc), static_cast<const T*>(vc), bt, max_blocks, lens, B,
@@ -481,7 +514,7 @@ extern "C" int pa_decode(void* out, const void* q, const void* k_cache, const vo
   const int64_t parts = parts_for(max_context_len, part);
   if (parts > 0x7fffffff) return PA_ERR_INVALID_ARG;
   const size_t need = ws_bytes(num_seqs, num_heads, head_dim, parts);
-  if (static_cast<int64_t>(parts) * num_kv_heads * num_seqs + kXcds > 0x7fffffffLL)
+  if (static_cast<int64_t>(parts) * num_kv_heads * num_seqs > 0x7fffffffLL)
     return PA_ERR_INVALID_ARG;
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_ERR_WORKSPACE;
   const int G = num_heads / num_kv_heads;

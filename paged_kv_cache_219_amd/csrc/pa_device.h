@@ -16,16 +16,16 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+// fp32 -> bf16 bits, round to nearest even (the hardware conversion,
+// v_cvt_pk_bf16_f32 on gfx950; NaN stays NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
-  uint32_t u = __builtin_bit_cast(uint32_t, x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u | ((u >> 16) & 0x8000u);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
 // Two fp32 -> packed bf16 pair (lo in bits 0..15), round to nearest even.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Low / high bf16 of a packed pair, widened exactly to fp32.

@@ -6,21 +6,30 @@
 // order, each chunk's KV accumulating in paged blocks; prefill is the
 // compute-heavy phase.  A chunk of n_q queries against L cached-plus-chunk
 // tokens is a dense contraction, so it runs on MFMA
-// (v_mfma_f32_16x16x32_bf16, fp32 accumulation).
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
 //
 // Causal alignment: query i of the chunk sits at position L - n_q + i and
 // attends to positions 0 .. L - n_q + i.
 //
-// Formulation (per wave: 16 query rows of one head):
-//   S^T = K Q^T   A = 16 tokens x 32 dims of K (one 1 KB run of the x-packed
-//                 key page), B = 32 dims x 16 queries (registers)
-//   O^T += V^T P^T   A = 16 dims x 32 tokens of V (d-major value page),
-//                 B = P^T straight from the S^T accumulators.
-// With the accumulator layout of a 16x16 MFMA (lane i holds column i%16, rows
-// 4*(i/16)..+3) every lane owns one query column, so the online softmax state
-// of a query lives in the four lanes i%16 == q and the 32-token P^T operand
-// is assembled in registers: slot k of lane group g is token 4g+k (k<4) of the
-// first page and 16+4g+(k-4) of the second; V^T uses the same token order.
+// Work decomposition.  A workgroup of 4 waves owns 128 consecutive query rows
+// of one (sequence, head); each wave owns 32 of them.  The workgroup walks the
+// keys/values in steps of 32 tokens (two 16-token pages): each step's K and V
+// pages are copied once, cooperatively, into double-buffered LDS (the next
+// step's copy is in flight while the current one is used), then every wave
+// computes, in transposed form so no operand needs a shuffle,
+//   S^T[32 tokens x 32 queries] = K Q^T    (8 MFMAs over head_dim 128)
+//   O^T[128 dims x 32 queries] += V^T P^T  (8 MFMAs)
+// With the 32x32 accumulator layout (lane l holds column l%32, rows
+// 8*(j/4) + 4*(l/32) + j%4 for j = 0..15), each lane owns one query column:
+// the online softmax of a query lives in lanes q and q+32, and the bf16 P^T
+// operand is built in registers from the lane's own scores.  V^T's operand
+// uses the same token order.  O is rescaled only when a query's running max
+// grows by more than 2^8 (the exponentials then stay below 2^8, far inside
+// fp32 and bf16 range; the final O / l is unchanged).
+//
+// Workgroups are mapped so the q-tiles of one (sequence, head) run on the same
+// XCD at the same time: its K/V pages come from HBM once and are served to the
+// other q-tiles from that XCD's L2.
 
 #include "pa_device.h"
 
@@ -28,166 +37,219 @@ namespace {
 
 constexpr int kBS = 16;
 constexpr int kD = 128;
-constexpr int kWavesPerWG = 4;
-constexpr int kRowsPerWave = 16;
+constexpr int kWaves = 4;
+constexpr int kRowsPerWave = 32;
+constexpr int kRowsPerWG = kWaves * kRowsPerWave;
+constexpr int kStep = 2 * kBS;        // tokens per step (two pages)
+constexpr int kPageElems = kBS * kD;  // elements of one (block, head) page
+constexpr uint32_t kXcds = 8;
+constexpr float kLazyRescale = 8.f;   // log2 units
 
-__device__ __forceinline__ pa::bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(pa::bf16x8_t, v); }
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ pa::f32x4_t mfma16(uint4 a, uint4 b, pa::f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+__device__ __forceinline__ pa::f32x16_t mfma32(uint4 a, uint4 b, pa::f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float xgroup_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  return fmaxf(v, __shfl_xor(v, 32, 64));
-}
-__device__ __forceinline__ float xgroup_sum(float v) {
-  v += __shfl_xor(v, 16, 64);
-  return v + __shfl_xor(v, 32, 64);
-}
+__device__ __forceinline__ float swap32_max(float v) { return fmaxf(v, __shfl_xor(v, 32, 64)); }
 
-// grid (ceil(max_query_len / 64), num_heads, num_seqs), 256 threads.
-__global__ __launch_bounds__(256) void prefill_chunk_kernel(
+// LDS layout of one step buffer (bf16 elements):
+//   K: [page 2][chunk 16][token 16][8]   -- the global page layout, two pages
+//   V: [page 2][dim 128][4 chunks of 4 tokens], the 8-byte chunks of each dim
+//      row stored at position chunk ^ ((dim / 8) % 4) so the V^T operand reads
+//      (32 dims x one chunk) hit 32 distinct bank pairs.
+struct StepBuf {
+  uint4 k[2 * kPageElems / 8];
+  uint2 v[2 * kPageElems / 4];
+};
+
+__device__ __forceinline__ int vswz(int d, int c8) { return d * 4 + (c8 ^ ((d >> 3) & 3)); }
+
+// grid (ceil(max_query_len / 128) * num_heads * num_seqs rounded up to 8), 256 threads.
+__global__ __launch_bounds__(256, 2) void prefill_chunk_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ block_tables, int32_t max_blocks,
-    const int32_t* __restrict__ qsl, const int32_t* __restrict__ context_lens, int32_t num_heads,
-    int32_t num_kv_heads, float scale_log2) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int h = blockIdx.y;
-  const int s = blockIdx.z;
+    const int32_t* __restrict__ qsl, const int32_t* __restrict__ context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t num_qtiles, float scale_log2) {
+  __shared__ StepBuf buf[2];
+
+  // XCD-aware order: logical = (seq, head, q-tile) with q-tile fastest, and XCD
+  // x runs the x-th contiguous slice, so a (seq, head)'s q-tiles share an L2.
+  const uint32_t per_xcd = gridDim.x / kXcds;
+  const uint32_t li = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  const int qt = num_qtiles - 1 - static_cast<int>(li % num_qtiles);  // long q-tiles first
+  const uint32_t sh = li / num_qtiles;
+  const int h = static_cast<int>(sh % static_cast<uint32_t>(num_heads));
+  const int s = static_cast<int>(sh / static_cast<uint32_t>(num_heads));
+  if (s >= num_seqs) return;  // grid padding (whole workgroup)
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = h / (num_heads / num_kv_heads);
   const int q0 = qsl[s];
   const int n_q = qsl[s + 1] - q0;
   const int L = context_lens[s];
-  const int row_a = blockIdx.x * (kWavesPerWG * kRowsPerWave) + wave * kRowsPerWave;
-  if (row_a >= n_q) return;
-  const int first_pos = L - n_q;  // position of query row 0
+  const int wg_row0 = qt * kRowsPerWG;
+  if (wg_row0 >= n_q) return;  // whole workgroup idle
+  const int first_pos = L - n_q;                  // position of chunk row 0
+  const int wg_last = first_pos + min(wg_row0 + kRowsPerWG, n_q) - 1;
+  const int nsteps = wg_last / kStep + 1;         // steps covering tokens 0 .. wg_last
 
-  const int qc = lane & 15;  // this lane's query column
-  const int grp = lane >> 4;
-  const int my_row = min(row_a + qc, n_q - 1);  // rows past the chunk mirror the last one
+  const int row0 = wg_row0 + wave * kRowsPerWave;
+  const bool wave_active = row0 < n_q;
+  const int qn = lane & 31;   // this lane's query column
+  const int hh = lane >> 5;   // which half of the accumulator rows
+  const int my_row = min(row0 + qn, n_q - 1);
   const int my_pos = first_pos + my_row;
-  const int last_pos = first_pos + min(row_a + kRowsPerWave, n_q) - 1;
-  const int first_row_pos = first_pos + row_a;
+  const int wave_last = first_pos + min(row0 + kRowsPerWave, n_q) - 1;
+  const int wave_first = first_pos + row0;
 
-  // Q^T operand: lane (qc, grp) holds dims 32*kk + 8*grp .. +7 of its query.
-  uint4 qreg[4];
+  // Q^T operand: lane (qn, hh) holds dims 16*kk + 8*hh .. +7 of its query row.
+  uint4 qreg[8];
   {
-    const uint16_t* qrow = q + (static_cast<int64_t>(q0 + my_row) * num_heads + h) * kD;
+    const uint16_t* qrow = q + (static_cast<int64_t>(q0 + my_row) * num_heads + h) * kD + 8 * hh;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      qreg[kk] = *reinterpret_cast<const uint4*>(qrow + 32 * kk + 8 * grp);
+    for (int kk = 0; kk < 8; ++kk) qreg[kk] = *reinterpret_cast<const uint4*>(qrow + 16 * kk);
   }
 
   const int32_t* bt_row = block_tables + static_cast<int64_t>(s) * max_blocks;
-  const int64_t page = static_cast<int64_t>(kBS) * kD;
-  const int64_t blk_stride = static_cast<int64_t>(num_kv_heads) * page;
-  const int64_t head_off = static_cast<int64_t>(g) * page;
+  const int64_t blk_stride = static_cast<int64_t>(num_kv_heads) * kPageElems;
+  const int64_t head_off = static_cast<int64_t>(g) * kPageElems;
 
-  pa::f32x4_t o[8];
+  // Cooperative copy of one step (2 pages of K and V = 16 KB): thread tid moves
+  // 16-byte units tid and tid + 256 of each.
+  uint4 kst[2], vst[2];
+  auto fetch = [&](int step) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = pa::f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < 2; ++r) {
+      const int u = tid + 256 * r;      // 16-byte unit within the two pages
+      const int page = u >> 8;          // 256 units per page
+      const int lb = step * 2 + page;
+      const int phys = lb * kBS <= wg_last ? bt_row[lb] : -1;
+      if (phys >= 0) {
+        const int64_t base = phys * blk_stride + head_off + (u & 255) * 8;
+        kst[r] = *reinterpret_cast<const uint4*>(kc + base);
+        vst[r] = *reinterpret_cast<const uint4*>(vc + base);
+      } else {
+        kst[r] = make_uint4(0, 0, 0, 0);
+        vst[r] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto stash = [&](int step, int b) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int u = tid + 256 * r;
+      buf[b].k[u] = kst[r];
+      // value unit = 8 tokens of one dim; zero the tokens at or past L (the
+      // cache may hold NaN there, and 0 * NaN would reach every query)
+      const int keep = L - ((step * 2 + (u >> 8)) * kBS + 8 * (u & 1));
+      if (keep < 8) {
+        uint32_t w[4] = {vst[r].x, vst[r].y, vst[r].z, vst[r].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          w[i] &= (2 * i < keep ? 0x0000ffffu : 0u) | (2 * i + 1 < keep ? 0xffff0000u : 0u);
+        vst[r] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+      // V unit u: page u>>8, dim (u & 255) >> 1, tokens 8*(u&1) .. +7 = chunks 2*(u&1), +1
+      const int page = u >> 8, d = (u & 255) >> 1, c8 = 2 * (u & 1);
+      uint2* vrow = buf[b].v + page * (kD * 4);
+      vrow[vswz(d, c8)] = make_uint2(vst[r].x, vst[r].y);
+      vrow[vswz(d, c8 + 1)] = make_uint2(vst[r].z, vst[r].w);
+    }
+  };
+
+  pa::f32x16_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = pa::f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int kv_end = last_pos + 1;  // tokens 0 .. last_pos are needed
-  for (int t0 = 0; t0 < kv_end; t0 += 2 * kBS) {
-    int phys[2];
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int lb = t0 / kBS + p;
-      phys[p] = lb * kBS < kv_end ? bt_row[lb] : -1;
-    }
-    // ---- S^T for two pages
-    pa::f32x4_t sacc[2];
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      sacc[p] = pa::f32x4_t{0.f, 0.f, 0.f, 0.f};
-      if (phys[p] >= 0) {
-        const uint16_t* kp = kc + phys[p] * blk_stride + head_off;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          // chunk c = 4*kk + grp of token qc: byte run (c*16 + qc) * 16
-          const uint4 a = *reinterpret_cast<const uint4*>(kp + ((4 * kk + grp) * kBS + qc) * 8);
-          sacc[p] = mfma16(a, qreg[kk], sacc[p]);
-        }
-      }
-    }
-    // ---- mask + online softmax (lane's query column)
-    const bool need_mask = t0 + 2 * kBS - 1 > first_row_pos || t0 + 2 * kBS > L;
-    float sv[8];
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = t0 + 16 * p + 4 * grp + r;
-        float x = sacc[p][r] * scale_log2;
-        if (need_mask && (t > my_pos || t >= L || phys[p] < 0)) x = -INFINITY;
-        sv[4 * p + r] = x;
-      }
-    float mt = sv[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sv[i]);
-    mt = xgroup_max(mt);
-    const float m_new = fmaxf(m_run, mt);
-    // a query with every token so far masked keeps m = -inf; guard the rescale
-    const float alpha = m_new == -INFINITY ? 1.f : pa::fast_exp2(m_run - m_new);
-    float pv[8];
-    float lsum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pv[i] = m_new == -INFINITY ? 0.f : pa::fast_exp2(sv[i] - m_new);
-      lsum += pv[i];
-    }
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] *= alpha;
-    // P^T operand: slots 0..3 = page 0 tokens 4grp..+3, 4..7 = page 1 tokens 4grp..+3
-    uint4 pb;
-    pb.x = pa::pack_bf16x2(pv[0], pv[1]);
-    pb.y = pa::pack_bf16x2(pv[2], pv[3]);
-    pb.z = pa::pack_bf16x2(pv[4], pv[5]);
-    pb.w = pa::pack_bf16x2(pv[6], pv[7]);
+  fetch(0);
+  stash(0, 0);
+  __syncthreads();
 
-    // ---- O^T += V^T P^T over 8 tiles of 16 dims
-    const bool tail = t0 + 2 * kBS > L;
+  for (int step = 0; step < nsteps; ++step) {
+    const int b = step & 1;
+    const bool more = step + 1 < nsteps;
+    if (more) fetch(step + 1);
+    const int t0 = step * kStep;
+
+    if (wave_active && t0 <= wave_last) {
+      // ---- S^T = K Q^T
+      pa::f32x16_t sacc = pa::f32x16_t{};
+      const int m = lane & 31;  // token row of the K operand
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const int d = 16 * dt + qc;
-      uint2 v0 = make_uint2(0, 0), v1 = make_uint2(0, 0);
-      if (phys[0] >= 0)
-        v0 = *reinterpret_cast<const uint2*>(vc + phys[0] * blk_stride + head_off + d * kBS + 4 * grp);
-      if (phys[1] >= 0)
-        v1 = *reinterpret_cast<const uint2*>(vc + phys[1] * blk_stride + head_off + d * kBS + 4 * grp);
-      if (tail) {
-        // zero value elements of tokens at or past L (the cache may hold NaN)
-        uint32_t w[4] = {v0.x, v0.y, v1.x, v1.y};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tb = t0 + 16 * (i >> 1) + 4 * grp + 2 * (i & 1);
-          const uint32_t mk = (tb < L ? 0x0000ffffu : 0u) | (tb + 1 < L ? 0xffff0000u : 0u);
-          w[i] &= mk;
-        }
-        v0 = make_uint2(w[0], w[1]);
-        v1 = make_uint2(w[2], w[3]);
+      for (int kk = 0; kk < 8; ++kk) {
+        const uint4 a = buf[b].k[((m >> 4) * 16 + 2 * kk + hh) * 16 + (m & 15)];
+        sacc = mfma32(a, qreg[kk], sacc);
       }
-      const uint4 a = make_uint4(v0.x, v0.y, v1.x, v1.y);
-      o[dt] = mfma16(a, pb, o[dt]);
+      // ---- online softmax over this lane's 16 tokens (query qn)
+      const bool need_mask = t0 + kStep - 1 > wave_first || t0 + kStep > L;
+      float x[16];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        x[j] = sacc[j] * scale_log2;
+        if (need_mask) {
+          const int t = t0 + 8 * (j >> 2) + 4 * hh + (j & 3);
+          if (t > my_pos || t >= L) x[j] = -INFINITY;
+        }
+        mx = fmaxf(mx, x[j]);
+      }
+      mx = swap32_max(mx);
+      if (mx > m_run + kLazyRescale) {  // identical in both halves of a query
+        const float alpha = pa::fast_exp2(m_run - mx);
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] *= alpha;
+        m_run = mx;
+      }
+      uint32_t pw[8];
+      float ls = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) {
+        const float p0 = pa::fast_exp2(x[j] - m_run);
+        const float p1 = pa::fast_exp2(x[j + 1] - m_run);
+        ls += p0 + p1;
+        pw[j >> 1] = pa::pack_bf16x2(p0, p1);
+      }
+      l_run += ls;
+      const uint4 pb0 = make_uint4(pw[0], pw[1], pw[2], pw[3]);  // tokens 0..15
+      const uint4 pb1 = make_uint4(pw[4], pw[5], pw[6], pw[7]);  // tokens 16..31
+      // ---- O^T += V^T P^T: A lane (dim, hh) holds tokens 4hh..+3 and 8+4hh..+3
+      // of page 0 (first MFMA) or page 1 (second), matching P^T's slots.
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int d = dt * 32 + (lane & 31);
+#pragma unroll
+        for (int page = 0; page < 2; ++page) {
+          const uint2* vrow = buf[b].v + page * (kD * 4);
+          const uint2 lo = vrow[vswz(d, hh)];
+          const uint2 hi = vrow[vswz(d, 2 + hh)];
+          o[dt] = mfma32(make_uint4(lo.x, lo.y, hi.x, hi.y), page ? pb1 : pb0, o[dt]);
+        }
+      }
     }
+    if (more) stash(step + 1, b ^ 1);
+    __syncthreads();
   }
 
-  const float lt = xgroup_sum(l_run);
+  if (!wave_active) return;
+  const float lt = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (row_a + qc < n_q) {
-    uint16_t* orow = out + (static_cast<int64_t>(q0 + row_a + qc) * num_heads + h) * kD;
+  if (row0 + qn < n_q) {
+    uint16_t* orow = out + (static_cast<int64_t>(q0 + row0 + qn) * num_heads + h) * kD;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      uint2 w;
-      w.x = pa::pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
-      w.y = pa::pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
-      *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * grp) = w;
-    }
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        uint2 w;
+        w.x = pa::pack_bf16x2(o[dt][4 * jg] * inv, o[dt][4 * jg + 1] * inv);
+        w.y = pa::pack_bf16x2(o[dt][4 * jg + 2] * inv, o[dt][4 * jg + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + dt * 32 + 8 * jg + 4 * hh) = w;
+      }
   }
 }
 
@@ -212,14 +274,16 @@ extern "C" int pa_prefill_chunk(void* out, const void* q, const void* k_cache,
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out) |
        reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache)) & 15)
     return PA_ERR_INVALID_ARG;
-  if (num_seqs > 65535 || num_heads > 65535) return PA_ERR_INVALID_ARG;
-  const int rows = kWavesPerWG * kRowsPerWave;
-  const uint32_t gx = static_cast<uint32_t>((static_cast<int64_t>(max_query_len) + rows - 1) / rows);
+  const int64_t qtiles = (static_cast<int64_t>(max_query_len) + kRowsPerWG - 1) / kRowsPerWG;
+  const int64_t wgs = qtiles * num_heads * num_seqs;
+  const int64_t grid = (wgs + kXcds - 1) / kXcds * kXcds;
+  if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
   const float sl2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
-  hipLaunchKernelGGL(prefill_chunk_kernel, dim3(gx, num_heads, num_seqs), dim3(256), 0,
+  hipLaunchKernelGGL(prefill_chunk_kernel, dim3(static_cast<uint32_t>(grid)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), static_cast<uint16_t*>(out),
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
                      static_cast<const uint16_t*>(v_cache), block_tables, max_blocks_per_seq,
-                     query_start_loc, context_lens, num_heads, num_kv_heads, sl2);
+                     query_start_loc, context_lens, num_seqs, num_heads, num_kv_heads,
+                     static_cast<int32_t>(qtiles), sl2);
   return pa_launch_status();
 }
