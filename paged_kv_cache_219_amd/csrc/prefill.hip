@@ -40,7 +40,9 @@ constexpr int kD = 128;
 constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 32;
 constexpr int kRowsPerWG = kWaves * kRowsPerWave;
-constexpr int kStep = 2 * kBS;        // tokens per step (two pages)
+constexpr int kPages = 2;             // pages per step
+constexpr int kRing = 4;              // LDS step buffers (loads run kRing-1 steps ahead)
+constexpr int kStep = kPages * kBS;   // tokens per step
 constexpr int kPageElems = kBS * kD;  // elements of one (block, head) page
 constexpr uint32_t kXcds = 8;
 constexpr float kLazyRescale = 8.f;   // log2 units
@@ -54,17 +56,36 @@ __device__ __forceinline__ pa::f32x16_t mfma32(uint4 a, uint4 b, pa::f32x16_t c)
 
 __device__ __forceinline__ float swap32_max(float v) { return fmaxf(v, __shfl_xor(v, 32, 64)); }
 
-// LDS layout of one step buffer (bf16 elements):
-//   K: [page 2][chunk 16][token 16][8]   -- the global page layout, two pages
-//   V: [page 2][dim 128][4 chunks of 4 tokens], the 8-byte chunks of each dim
-//      row stored at position chunk ^ ((dim / 8) % 4) so the V^T operand reads
-//      (32 dims x one chunk) hit 32 distinct bank pairs.
+// LDS layout of one step buffer, in 16-byte units:
+//   K: [page][chunk 16][token 16]  -- the global page layout
+//   V: [page][dim 128][2 halves of 8 tokens], the two halves of each dim row
+//      swapped when (dim / 8) is odd, so the V^T operand reads (32 dims x 8
+//      bytes) hit distinct bank pairs.
+// Steps are copied with direct-to-LDS loads (lane i of a wave instruction
+// lands at base + 16 i), each lane fetching the global unit that belongs at its
+// LDS position.
 struct StepBuf {
-  uint4 k[2 * kPageElems / 8];
-  uint2 v[2 * kPageElems / 4];
+  uint4 k[kPages * 256];
+  uint4 v[kPages * 256];
 };
 
-__device__ __forceinline__ int vswz(int d, int c8) { return d * 4 + (c8 ^ ((d >> 3) & 3)); }
+__device__ __forceinline__ int vhalf(int d, int half) { return half ^ ((d >> 3) & 1); }
+
+// 16-byte direct-to-LDS load: lane i's bytes land at LDS byte address
+// lds_base + 16 i.  Issued through asm so the compiler does not pair every
+// later LDS read with a wait for all outstanding copies; the kernel waits for
+// them explicitly (vmcnt) before the barrier that publishes a step.
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds_base)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
+}
 
 // grid (ceil(max_query_len / 128) * num_heads * num_seqs rounded up to 8), 256 threads.
 __global__ __launch_bounds__(256, 2) void prefill_chunk_kernel(
@@ -72,7 +93,7 @@ __global__ __launch_bounds__(256, 2) void prefill_chunk_kernel(
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ block_tables, int32_t max_blocks,
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ context_lens, int32_t num_seqs,
     int32_t num_heads, int32_t num_kv_heads, int32_t num_qtiles, float scale_log2) {
-  __shared__ StepBuf buf[2];
+  __shared__ StepBuf buf[kRing];
 
   // XCD-aware order: logical = (seq, head, q-tile) with q-tile fastest, and XCD
   // x runs the x-th contiguous slice, so a (seq, head)'s q-tiles share an L2.
@@ -112,52 +133,62 @@ __global__ __launch_bounds__(256, 2) void prefill_chunk_kernel(
     const uint16_t* qrow = q + (static_cast<int64_t>(q0 + my_row) * num_heads + h) * kD + 8 * hh;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) qreg[kk] = *reinterpret_cast<const uint4*>(qrow + 16 * kk);
+    // Consume the query registers here: otherwise their load waits land in
+    // the step loop, where (loads retiring in order) they would also drain
+    // every step copy in flight.
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      asm volatile("" : "+v"(qreg[kk].x), "+v"(qreg[kk].y), "+v"(qreg[kk].z), "+v"(qreg[kk].w));
   }
 
   const int32_t* bt_row = block_tables + static_cast<int64_t>(s) * max_blocks;
   const int64_t blk_stride = static_cast<int64_t>(num_kv_heads) * kPageElems;
   const int64_t head_off = static_cast<int64_t>(g) * kPageElems;
 
-  // Cooperative copy of one step (2 pages of K and V = 16 KB): thread tid moves
-  // 16-byte units tid and tid + 256 of each.
-  uint4 kst[2], vst[2];
-  auto fetch = [&](int step) {
+  // Each wave copies 2 x 1 KB of K and 2 x 1 KB of V per step (the step is
+  // 2 pages = 8 KB of each).  Unit u = 128 * wave + 64 * i + lane.  Pages past
+  // the last needed token load logical block 0 instead (always valid): their
+  // scores are masked, and their values must just be finite.
+  auto issue = [&](int step) {
+    StepBuf& B = buf[step % kRing];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int u = tid + 256 * r;      // 16-byte unit within the two pages
-      const int page = u >> 8;          // 256 units per page
-      const int lb = step * 2 + page;
-      const int phys = lb * kBS <= wg_last ? bt_row[lb] : -1;
-      if (phys >= 0) {
-        const int64_t base = phys * blk_stride + head_off + (u & 255) * 8;
-        kst[r] = *reinterpret_cast<const uint4*>(kc + base);
-        vst[r] = *reinterpret_cast<const uint4*>(vc + base);
-      } else {
-        kst[r] = make_uint4(0, 0, 0, 0);
-        vst[r] = make_uint4(0, 0, 0, 0);
-      }
+    for (int i = 0; i < 2; ++i) {
+      const int u0 = 128 * wave + 64 * i;  // wave-uniform base unit
+      const int u = u0 + lane;
+      const int page = u0 >> 8;            // a 64-unit run never crosses a page
+      const int lb = step * kPages + page;
+      const int phys = bt_row[lb * kBS <= wg_last ? lb : 0];
+      const uint16_t* kp = kc + phys * blk_stride + head_off;
+      const uint16_t* vp = vc + phys * blk_stride + head_off;
+      const int pos = u & 255;
+      const int d = pos >> 1;
+      lds_dma16(kp + pos * 8, __builtin_amdgcn_readfirstlane(lds_addr(&B.k[u0])));
+      lds_dma16(vp + (d * 2 + vhalf(d, pos & 1)) * 8,
+                __builtin_amdgcn_readfirstlane(lds_addr(&B.v[u0])));
     }
   };
-  auto stash = [&](int step, int b) {
+  // Values of tokens at or past L in the step's last page: zero them in LDS
+  // (the cache may hold NaN there, and 0 * NaN would reach every query).
+  auto zero_tail = [&](int step) {
+    StepBuf& B = buf[step % kRing];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const int u = tid + 256 * r;
-      buf[b].k[u] = kst[r];
-      // value unit = 8 tokens of one dim; zero the tokens at or past L (the
-      // cache may hold NaN there, and 0 * NaN would reach every query)
-      const int keep = L - ((step * 2 + (u >> 8)) * kBS + 8 * (u & 1));
-      if (keep < 8) {
-        uint32_t w[4] = {vst[r].x, vst[r].y, vst[r].z, vst[r].w};
+      const int row = tid + 256 * r;      // (page, dim) row, 2 units each
+      const int page = row >> 7, d = row & 127;
+      const int tok0 = (step * kPages + page) * kBS;
+      uint4* vr = &B.v[page * 256 + d * 2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          w[i] &= (2 * i < keep ? 0x0000ffffu : 0u) | (2 * i + 1 < keep ? 0xffff0000u : 0u);
-        vst[r] = make_uint4(w[0], w[1], w[2], w[3]);
+      for (int half = 0; half < 2; ++half) {
+        const int keep = L - (tok0 + 8 * half);
+        if (keep < 8) {
+          uint4& w4 = vr[vhalf(d, half)];
+          uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            w[i] &= (2 * i < keep ? 0x0000ffffu : 0u) | (2 * i + 1 < keep ? 0xffff0000u : 0u);
+          w4 = make_uint4(w[0], w[1], w[2], w[3]);
+        }
       }
-      // V unit u: page u>>8, dim (u & 255) >> 1, tokens 8*(u&1) .. +7 = chunks 2*(u&1), +1
-      const int page = u >> 8, d = (u & 255) >> 1, c8 = 2 * (u & 1);
-      uint2* vrow = buf[b].v + page * (kD * 4);
-      vrow[vswz(d, c8)] = make_uint2(vst[r].x, vst[r].y);
-      vrow[vswz(d, c8 + 1)] = make_uint2(vst[r].z, vst[r].w);
     }
   };
 
@@ -166,74 +197,92 @@ __global__ __launch_bounds__(256, 2) void prefill_chunk_kernel(
   for (int i = 0; i < 4; ++i) o[i] = pa::f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  fetch(0);
-  stash(0, 0);
-  __syncthreads();
+  for (int st = 0; st < kRing - 1 && st < nsteps; ++st) issue(st);
 
   for (int step = 0; step < nsteps; ++step) {
-    const int b = step & 1;
-    const bool more = step + 1 < nsteps;
-    if (more) fetch(step + 1);
+    const StepBuf& B = buf[step % kRing];
+    // wait for this wave's copies of this step (later steps may stay in
+    // flight), then for everyone's
+    const int ahead = min(kRing - 2, nsteps - 1 - step);
+    if (ahead >= 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if (ahead == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     const int t0 = step * kStep;
+    if (t0 + kStep > L) {  // the step holding the sequence's last token
+      zero_tail(step);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
+    // the buffer written next was last read in the previous step, which every
+    // wave has finished (barrier above)
+    if (step + kRing - 1 < nsteps) issue(step + kRing - 1);
 
     if (wave_active && t0 <= wave_last) {
       // ---- S^T = K Q^T
-      pa::f32x16_t sacc = pa::f32x16_t{};
+      pa::f32x16_t sa = pa::f32x16_t{};
       const int m = lane & 31;  // token row of the K operand
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        const uint4 a = buf[b].k[((m >> 4) * 16 + 2 * kk + hh) * 16 + (m & 15)];
-        sacc = mfma32(a, qreg[kk], sacc);
+        const uint4 a0 = B.k[((m >> 4) * 16 + 2 * kk + hh) * 16 + (m & 15)];
+        sa = mfma32(a0, qreg[kk], sa);
       }
-      // ---- online softmax over this lane's 16 tokens (query qn)
-      const bool need_mask = t0 + kStep - 1 > wave_first || t0 + kStep > L;
+      // ---- online softmax over this lane's 16 tokens (query qn).  Token of
+      // element j: t0 + 8*(j/4) + 4*hh + j%4.
       float x[16];
-      float mx = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        x[j] = sacc[j] * scale_log2;
-        if (need_mask) {
-          const int t = t0 + 8 * (j >> 2) + 4 * hh + (j & 3);
-          if (t > my_pos || t >= L) x[j] = -INFINITY;
+      for (int j = 0; j < 16; ++j) x[j] = sa[j];
+      if (t0 + kStep - 1 > wave_first || t0 + kStep > L) {  // diagonal or tail step
+        const int lim = min(my_pos, L - 1) - t0 - 4 * hh;   // keep offsets <= lim
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int off = 8 * (j >> 2) + (j & 3);
+          if (off > lim) x[j] = -INFINITY;
         }
-        mx = fmaxf(mx, x[j]);
       }
-      mx = swap32_max(mx);
-      if (mx > m_run + kLazyRescale) {  // identical in both halves of a query
-        const float alpha = pa::fast_exp2(m_run - mx);
+      float mx = fmaxf(x[0], x[1]);
+#pragma unroll
+      for (int j = 2; j < 16; j += 2) mx = fmaxf(mx, fmaxf(x[j], x[j + 1]));
+      mx = swap32_max(mx) * scale_log2;  // scale > 0: max commutes with it
+      // Lazy rescale, wave-uniform: only when some query's max grew by > 2^8.
+      if (__any(mx > m_run + kLazyRescale)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = pa::fast_exp2(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] *= alpha;
-        m_run = mx;
+        m_run = m_new;
       }
+      const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
       uint32_t pw[8];
       float ls = 0.f;
 #pragma unroll
       for (int j = 0; j < 16; j += 2) {
-        const float p0 = pa::fast_exp2(x[j] - m_run);
-        const float p1 = pa::fast_exp2(x[j + 1] - m_run);
+        const float p0 = pa::fast_exp2(fmaf(x[j], scale_log2, neg_m));
+        const float p1 = pa::fast_exp2(fmaf(x[j + 1], scale_log2, neg_m));
         ls += p0 + p1;
         pw[j >> 1] = pa::pack_bf16x2(p0, p1);
       }
       l_run += ls;
-      const uint4 pb0 = make_uint4(pw[0], pw[1], pw[2], pw[3]);  // tokens 0..15
-      const uint4 pb1 = make_uint4(pw[4], pw[5], pw[6], pw[7]);  // tokens 16..31
-      // ---- O^T += V^T P^T: A lane (dim, hh) holds tokens 4hh..+3 and 8+4hh..+3
-      // of page 0 (first MFMA) or page 1 (second), matching P^T's slots.
+      // P^T operands, one per page: page pg's 16 tokens are the lane's
+      // elements 8*pg .. 8*pg+7 (tokens 4hh..+3 and 8+4hh..+3 of that page).
+      // ---- O^T += V^T P^T
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const int d = dt * 32 + (lane & 31);
+      for (int pg = 0; pg < kPages; ++pg) {
+        const uint4 pb = make_uint4(pw[4 * pg], pw[4 * pg + 1], pw[4 * pg + 2], pw[4 * pg + 3]);
 #pragma unroll
-        for (int page = 0; page < 2; ++page) {
-          const uint2* vrow = buf[b].v + page * (kD * 4);
-          const uint2 lo = vrow[vswz(d, hh)];
-          const uint2 hi = vrow[vswz(d, 2 + hh)];
-          o[dt] = mfma32(make_uint4(lo.x, lo.y, hi.x, hi.y), page ? pb1 : pb0, o[dt]);
+        for (int dt = 0; dt < 4; ++dt) {
+          const int d = dt * 32 + (lane & 31);
+          // tokens 4hh..+3 (half 0, byte 8*hh) and 8+4hh..+3 (half 1, byte 8*hh)
+          const uint2* r0 = reinterpret_cast<const uint2*>(&B.v[pg * 256 + d * 2 + vhalf(d, 0)]);
+          const uint2* r1 = reinterpret_cast<const uint2*>(&B.v[pg * 256 + d * 2 + vhalf(d, 1)]);
+          const uint2 lo = r0[hh], hi = r1[hh];
+          o[dt] = mfma32(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, o[dt]);
         }
       }
     }
-    if (more) stash(step + 1, b ^ 1);
-    __syncthreads();
   }
 
   if (!wave_active) return;
