@@ -21,7 +21,8 @@
 //  * QK, one token per lane: lane 16j+t owns token t of page j and loads that
 //    token's whole key row -- with the x-packed key layout the 16 lanes of a
 //    page read 256 contiguous bytes per load.  The G query heads sharing the
-//    kv head are broadcast from LDS; bf16 products use v_dot2_f32_bf16 (exact
+//    kv head are wave-uniform and read with scalar loads into SGPRs, which
+//    feed the dot products directly; bf16 products use v_dot2_f32_bf16 (exact
 //    products, fp32 accumulation), so no cross-lane reduction is needed for
 //    the dot products.
 //  * online softmax per head: wave max -> rescale factor 2^(m_old - m_new),
