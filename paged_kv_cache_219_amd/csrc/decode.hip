@@ -34,7 +34,9 @@
 // Tokens past the context are masked by selecting -inf scores and zeroing
 // their value elements (the cache may hold anything there).
 
-#include "pa_device.h"
+#include "page_ring.h"
+
+#include <type_traits>
 
 namespace {
 
@@ -143,8 +145,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   // through the constant address space turns them into scalar loads whose
   // SGPRs feed the dot products directly.
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  const __attribute__((address_space(4))) u32x4* q_const =
-      (const __attribute__((address_space(4))) u32x4*)(q + out_row);
+  typedef const __attribute__((address_space(4))) u32x4* q_ptr_t;
+  q_ptr_t q_const = (q_ptr_t)(q + out_row);
+  // More than 64 dwords of queries do not fit the scalar register file: the
+  // rows are then re-read (scalar cache hits) in every tile instead of being
+  // kept live across the loop.
+  constexpr bool kQReload = G * D * sizeof(T) > 256;
 
   const int32_t* bt_row = block_tables + static_cast<int64_t>(s) * max_blocks;
   const int64_t head_off = static_cast<int64_t>(g) * Gm::PAGE;
@@ -156,6 +162,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 
   uint4 kreg[NKC];
   uint4 vreg[4][NVI];
+#pragma unroll
+  for (int c = 0; c < NKC; ++c) kreg[c] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int k = 0; k < NVI; ++k) vreg[j][k] = make_uint4(0, 0, 0, 0);
   float m[G], l[G], acc[G][NVI];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -173,14 +185,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     const int lb = lb_part + tile * 4 + j;
     return lb * kBS < part_end ? bt_row[lb] : -1;
   };
+  // Pages past the end of the partition are not loaded: their registers keep
+  // stale contents, which no result uses (their scores are replaced by -inf
+  // and their value pages are skipped).
   auto load_k = [&](int phys, int kofs) {
     if (phys >= 0) {
       const T* base = kc + phys * blk_stride + head_off + kofs;
 #pragma unroll
       for (int c = 0; c < NKC; ++c) kreg[c] = ld16(base + c * (kBS * X));
-    } else {
-#pragma unroll
-      for (int c = 0; c < NKC; ++c) kreg[c] = make_uint4(0, 0, 0, 0);
     }
   };
   auto load_v = [&](const int (&ids)[4], int vofs) {
@@ -190,9 +202,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
         const T* base = vc + ids[j] * blk_stride + head_off + vofs;
 #pragma unroll
         for (int k = 0; k < NVI; ++k) vreg[j][k] = ld16(base + k * 64 * X);
-      } else {
-#pragma unroll
-        for (int k = 0; k < NVI; ++k) vreg[j][k] = make_uint4(0, 0, 0, 0);
       }
     }
   };
@@ -230,26 +239,44 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 
     // ---- scores, one token per lane
     float sc[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) sc[h] = 0.f;
-#pragma unroll
-    for (int c = 0; c < NKC; ++c) {
-      const uint4 kv = kreg[c];
+    auto dot_chunk = [&](float a, u32x4 qw, uint4 kv) -> float {
+      if (sizeof(T) == 2) {
+        a = pa::dot2_bf16(qw.x, kv.x, a);
+        a = pa::dot2_bf16(qw.y, kv.y, a);
+        a = pa::dot2_bf16(qw.z, kv.z, a);
+        a = pa::dot2_bf16(qw.w, kv.w, a);
+      } else {
+        a = fmaf(__uint_as_float(qw.x), __uint_as_float(kv.x), a);
+        a = fmaf(__uint_as_float(qw.y), __uint_as_float(kv.y), a);
+        a = fmaf(__uint_as_float(qw.z), __uint_as_float(kv.z), a);
+        a = fmaf(__uint_as_float(qw.w), __uint_as_float(kv.w), a);
+      }
+      return a;
+    };
+    if (kQReload) {
+      // One head at a time; the next head's query row is loaded once this
+      // head's scores are done (the address takes an empty asm dependency on
+      // them), so only one row occupies scalar registers.
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const u32x4 qw = q_const[h * NKC + c];  // wave-uniform: scalar loads
-        const uint4 qv = make_uint4(qw.x, qw.y, qw.z, qw.w);
-        if (sizeof(T) == 2) {
-          sc[h] = pa::dot2_bf16(qv.x, kv.x, sc[h]);
-          sc[h] = pa::dot2_bf16(qv.y, kv.y, sc[h]);
-          sc[h] = pa::dot2_bf16(qv.z, kv.z, sc[h]);
-          sc[h] = pa::dot2_bf16(qv.w, kv.w, sc[h]);
-        } else {
-          sc[h] = fmaf(__uint_as_float(qv.x), __uint_as_float(kv.x), sc[h]);
-          sc[h] = fmaf(__uint_as_float(qv.y), __uint_as_float(kv.y), sc[h]);
-          sc[h] = fmaf(__uint_as_float(qv.z), __uint_as_float(kv.z), sc[h]);
-          sc[h] = fmaf(__uint_as_float(qv.w), __uint_as_float(kv.w), sc[h]);
-        }
+        uint64_t qa = reinterpret_cast<uint64_t>(q_const + h * NKC);
+        if (h > 0)
+          asm volatile("" : "+s"(qa) : "v"(sc[h - 1]));
+        else
+          asm volatile("" : "+s"(qa));
+        const q_ptr_t qh = reinterpret_cast<q_ptr_t>(qa);
+        float a = 0.f;
+#pragma unroll
+        for (int c = 0; c < NKC; ++c) a = dot_chunk(a, qh[c], kreg[c]);
+        sc[h] = a;
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < G; ++h) sc[h] = 0.f;
+#pragma unroll
+      for (int c = 0; c < NKC; ++c) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) sc[h] = dot_chunk(sc[h], q_const[h * NKC + c], kreg[c]);
       }
     }
     int ids_next[4];
@@ -389,43 +416,299 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   }
 }
 
-// Second pass, one wave per (kv head, sequence) with more than one partition:
-// for each of the G heads, out = sum_p w_p o_p / sum_p w_p with
-// w_p = l_p * 2^(m_p - max_p m_p), partitions in order (deterministic).
-// (Merging inside the first pass would need an agent-scope release per
-// partition -- an L2 write-back on this chip, far costlier than this launch.)
-template <typename T, int D, int G>
-__global__ __launch_bounds__(64) void decode_merge_kernel(
-    T* __restrict__ out, Partials ws, const int32_t* __restrict__ context_lens, int32_t num_seqs,
-    int32_t num_heads, int32_t num_kv_heads, int32_t num_parts, int32_t partition) {
-  const int lane = threadIdx.x;
-  const int s = static_cast<int>(blockIdx.x % static_cast<uint32_t>(num_seqs));
-  const int g = static_cast<int>(blockIdx.x / static_cast<uint32_t>(num_seqs));
+// Grouped-query decode (4 or 8 query heads per kv head; bf16, head_dim 128).
+//
+// One 4-wave workgroup per (partition, sequence, kv head).  The partition's
+// pages stream through LDS in 32-token steps (page_ring.h: direct-to-LDS
+// copies three steps ahead, so up to 48 KB per workgroup is in flight while
+// the waves compute), and every wave reads the staged K/V for its own GW
+// query heads -- each page leaves HBM once for all G heads, and no K/V bytes
+// pass through registers before they are used.
+//
+// Per step and wave:
+//  * QK: lane = (token, half): token (lane / 2) of the step, dims
+//    64 * (lane % 2) .. +63 (8 chunks), so the 64 lanes cover 32 tokens x
+//    128 dims; the two halves are summed with one DPP exchange.  The lane's
+//    half of each query row sits in registers for the whole partition.
+//  * softmax with a lazily moved reference: the weights of a step are
+//    2^(s - m) for the wave-uniform reference m, and m (with the running sums
+//    and accumulators) only moves when some score exceeds it by more than
+//    2^8 -- rare after the first step, and the final o / l is unchanged.
+//  * PV: lane = (token group, dim): token group (lane / 16) = 8 tokens of
+//    one page, dims (lane % 16) + 16 k for k = 0..7; the group's 8 bf16
+//    weights per head come from this wave's LDS row and pair with the d-major
+//    value chunk in v_dot2_f32_bf16.  The four token groups are summed once,
+//    at the end.
+// Tokens past the partition's end are masked (-inf scores, zeroed value
+// chunks); pages wholly past it re-read the step's first page (served from
+// L2) so every wave issues the same number of copies per step.  Block ids of
+// the first 64 pages of the partition are read once, into one register.
+template <int GW, int R, int W>
+__device__ __forceinline__ void group_item(
+    uint32_t li, pa::ring::StepBuf (&buf)[R], uint4 (&p_lds)[W][GW][4],
+    uint16_t* __restrict__ out, Partials ws, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const int32_t* __restrict__ block_tables, int32_t max_blocks,
+    const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t num_parts, int32_t partition, float scale_log2) {
+  using namespace pa::ring;
+  constexpr int G = W * GW;
+  constexpr float kLazy = 8.f;  // log2 units
+
+  // same logical order as decode_kernel: kv head fastest, then sequence, then
+  // partition
+  const int g = static_cast<int>(li % static_cast<uint32_t>(num_kv_heads));
+  const uint32_t ps = li / static_cast<uint32_t>(num_kv_heads);
+  const int s = static_cast<int>(ps % static_cast<uint32_t>(num_seqs));
+  const int part = static_cast<int>(ps / static_cast<uint32_t>(num_seqs));
+  if (part >= num_parts) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h0 = g * G;
   const int L = context_lens[s];
-  const int n = (L + partition - 1) / partition;
-  if (n <= 1) return;
-  constexpr int PER = D / 64;
-#pragma unroll 1
-  for (int h = g * G; h < (g + 1) * G; ++h) {
-    const int64_t row0 = (static_cast<int64_t>(s) * num_heads + h) * num_parts;
-    float M = -INFINITY;
-    for (int p = 0; p < n; ++p) M = fmaxf(M, ws.ml[2 * (row0 + p)]);
-    float o[PER] = {};
-    float wsum = 0.f;
-    for (int p = 0; p < n; ++p) {
-      const float w = ws.ml[2 * (row0 + p) + 1] * pa::fast_exp2(ws.ml[2 * (row0 + p)] - M);
-      wsum += w;
+  const int part_start = part * partition;
+  const int64_t out_row = (static_cast<int64_t>(s) * num_heads + h0) * kD;
+  if (L <= 0) {
+    if (part == 0)
+      for (int i = tid; i < G * kD; i += W * 64) out[out_row + i] = 0;
+    return;
+  }
+  if (part_start >= L) return;
+  const int part_end = min(part_start + partition, L);
+  const int nparts_s = (L + partition - 1) / partition;
+  const int nsteps = (part_end - part_start + kStep - 1) / kStep;
+  const int npages = (part_end - part_start + kBS - 1) / kBS;
+  const int lb_part = part_start / kBS;
+
+  const int half = lane & 1;        // QK: which 64 dims
+  const int tok = lane >> 1;        // QK: token of the step
+  const int tg = lane >> 4;         // PV: token group (page tg / 2, tokens 8 * (tg % 2) ..)
+  const int dl = lane & 15;         // PV: dims dl + 16 k
+  const int hw = h0 + wave * GW;    // first query head of this wave
+
+  const int32_t* bt_row = block_tables + static_cast<int64_t>(s) * max_blocks;
+  int ids = bt_row[lb_part + min(lane, npages - 1)];  // block ids of pages 0..63
+  uint4 qreg[GW][8];
 #pragma unroll
-      for (int i = 0; i < PER; ++i) o[i] = fmaf(w, ws.o[(row0 + p) * D + i * 64 + lane], o[i]);
+  for (int h = 0; h < GW; ++h) {
+    const uint16_t* qrow = q + (static_cast<int64_t>(s) * num_heads + hw + h) * kD + 64 * half;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) qreg[h][c] = *reinterpret_cast<const uint4*>(qrow + 8 * c);
+  }
+  // consume these loads before the copies start (loads retire in order: a
+  // wait for them inside the loop would also drain the copies in flight)
+  asm volatile("" : "+v"(ids));
+#pragma unroll
+  for (int h = 0; h < GW; ++h)
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      asm volatile("" : "+v"(qreg[h][c].x), "+v"(qreg[h][c].y), "+v"(qreg[h][c].z),
+                   "+v"(qreg[h][c].w));
+
+  const int64_t blk_stride = static_cast<int64_t>(num_kv_heads) * kPageElems;
+  const int64_t head_off = static_cast<int64_t>(g) * kPageElems;
+  auto issue = [&](int step) {
+    int pi = step * kPages + page_of<W>(wave);  // page of the partition
+    if (pi >= npages) pi = step * kPages;  // past the end: the step's first page
+    const int phys = pi < 64 ? __builtin_amdgcn_readlane(ids, pi) : bt_row[lb_part + pi];
+    issue_step<W>(buf[step % R], kc, vc, phys, blk_stride, head_off, wave, lane);
+  };
+
+  float m[GW], lsum[GW], acc[GW][8];
+#pragma unroll
+  for (int h = 0; h < GW; ++h) {
+    m[h] = -INFINITY;
+    lsum[h] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[h][k] = 0.f;
+  }
+
+  for (int st = 0; st < R - 1 && st < nsteps; ++st) issue(st);
+
+  const int kofs = ((tok >> 4) * 16 + 8 * half) * 16;  // page and chunk base of the key reads
+  // One step; TAIL marks the last one, the only step that can hold tokens at
+  // or past the partition's end.
+  auto do_step = [&](int step, auto tail_tag) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    const StepBuf& B = buf[step % R];
+    wait_step<R, W>(min(R - 2, nsteps - 1 - step));
+    // the buffer written next was last read in the previous step, which every
+    // wave has finished (barrier above)
+    if (!TAIL && step + R - 1 < nsteps) issue(step + R - 1);
+    const int t0 = part_start + step * kStep;
+
+    // ---- scores
+    float sc[GW];
+#pragma unroll
+    for (int h = 0; h < GW; ++h) sc[h] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint4 kv = B.k[kofs + c * 16 + kslot(8 * half + c, tok & 15)];
+#pragma unroll
+      for (int h = 0; h < GW; ++h) {
+        float a = sc[h];
+        a = pa::dot2_bf16(qreg[h][c].x, kv.x, a);
+        a = pa::dot2_bf16(qreg[h][c].y, kv.y, a);
+        a = pa::dot2_bf16(qreg[h][c].z, kv.z, a);
+        a = pa::dot2_bf16(qreg[h][c].w, kv.w, a);
+        sc[h] = a;
+      }
     }
-    const float inv = 1.f / wsum;
-    T* dst = out + (static_cast<int64_t>(s) * num_heads + h) * D;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) store_out<T>(dst + i * 64 + lane, o[i] * inv);
+    for (int h = 0; h < GW; ++h) {
+      const float full = sc[h] + pa::dpp<pa::kDppXor1>(sc[h]);  // same bits in both lanes
+      float sv = full * scale_log2;
+      if (TAIL && t0 + tok >= part_end) sv = -INFINITY;
+      float m_new = m[h];
+      if (__any(sv > m[h] + kLazy)) m_new = fmaxf(m[h], pa::wave_max_u(sv));  // wave-uniform
+      // rescale unconditionally (by exactly 1 when the reference stays): a
+      // branch here would make the compiler copy every accumulator
+      const float alpha = m_new == m[h] ? 1.f : pa::fast_exp2(m[h] - m_new);
+      lsum[h] *= alpha;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[h][k] *= alpha;
+      m[h] = m_new;
+      const float p = pa::fast_exp2(sv - m[h]);
+      lsum[h] += p;  // every token counted twice (both halves)
+      reinterpret_cast<uint16_t*>(&p_lds[wave][h][0])[tok] =
+          static_cast<uint16_t>(pa::f32_to_bf16_bits(p));
+    }
+    lds_wave_sync();
+
+    // ---- weighted values
+    const int keep = part_end - (t0 + 8 * tg);  // valid tokens of this lane's group
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int d = dl + 16 * k;
+      uint4 vv = B.v[(tg >> 1) * 256 + d * 2 + vhalf(d, tg & 1)];
+      if (TAIL) vv = mask_chunk<uint16_t>(vv, keep);
+#pragma unroll
+      for (int h = 0; h < GW; ++h) {
+        const uint4 pw = p_lds[wave][h][tg];
+        float a = acc[h][k];
+        a = pa::dot2_bf16(pw.x, vv.x, a);
+        a = pa::dot2_bf16(pw.y, vv.y, a);
+        a = pa::dot2_bf16(pw.z, vv.z, a);
+        a = pa::dot2_bf16(pw.w, vv.w, a);
+        acc[h][k] = a;
+      }
+    }
+    lds_wave_sync();  // p_lds is rewritten by the next step
+  };
+  for (int step = 0; step < nsteps - 1; ++step) do_step(step, std::false_type{});
+  do_step(nsteps - 1, std::true_type{});
+
+  // ---- sum the four token groups; write the output or this partition's partial
+#pragma unroll
+  for (int h = 0; h < GW; ++h) {
+    const float lt = 0.5f * pa::wave_sum_u(lsum[h]);
+    const float inv = 1.f / lt;
+    const int head = hw + h;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      float a = acc[h][k];
+      a += __shfl_xor(a, 16, 64);
+      a += __shfl_xor(a, 32, 64);
+      const int d = dl + 16 * k;
+      if (tg == 0) {
+        if (nparts_s == 1) {
+          out[(static_cast<int64_t>(s) * num_heads + head) * kD + d] =
+              static_cast<uint16_t>(pa::f32_to_bf16_bits(a * inv));
+        } else {
+          const int64_t row = (static_cast<int64_t>(s) * num_heads + head) * num_parts + part;
+          ws.o[row * kD + d] = a * inv;
+        }
+      }
+    }
+    if (nparts_s > 1 && lane == 0) {
+      const int64_t row = (static_cast<int64_t>(s) * num_heads + head) * num_parts + part;
+      ws.ml[2 * row] = m[h];
+      ws.ml[2 * row + 1] = lt;
+    }
   }
 }
 
+// One workgroup per item (partition, sequence, kv head), in the one-wave
+// kernel's order.
+#ifndef PA_GROUP_RING
+#define PA_GROUP_RING 3
+#endif
+constexpr int kGroupRing = PA_GROUP_RING;  // 3 x 16 KB: three workgroups per CU
+
+template <int GW, int W>
+__global__ __launch_bounds__(W * 64) void decode_group_kernel(
+    uint16_t* __restrict__ out, Partials ws, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const int32_t* __restrict__ block_tables, int32_t max_blocks,
+    const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t num_parts, int32_t partition, float scale_log2) {
+  __shared__ pa::ring::StepBuf buf[kGroupRing];
+  __shared__ uint4 p_lds[W][GW][4];  // per wave and head: 32 bf16 weights
+  group_item<GW, kGroupRing, W>(blockIdx.x, buf, p_lds, out, ws, q, kc, vc, block_tables, max_blocks,
+                 context_lens, num_seqs, num_heads, num_kv_heads, num_parts, partition,
+                 scale_log2);
+}
+
+// Second pass, one wave per (sequence, query head) with more than one
+// partition: out = sum_p w_p o_p / sum_p w_p with w_p = l_p * 2^(m_p - M),
+// M = max_p m_p.  Lane p computes partition p's weight (64 partitions at a
+// time); the partial outputs are then accumulated in partition order, each
+// lane owning D/64 consecutive dimensions, so the result is deterministic.
+// (Merging inside the first pass would need an agent-scope release per
+// partition -- an L2 write-back on this chip, far costlier than this launch.)
+template <typename T, int D>
+__global__ __launch_bounds__(64) void decode_merge_kernel(
+    T* __restrict__ out, Partials ws, const int32_t* __restrict__ context_lens, int32_t num_heads,
+    int32_t num_parts, int32_t partition) {
+  constexpr int PER = D / 64;
+  typedef float vec_t __attribute__((ext_vector_type(PER)));
+  const int lane = threadIdx.x;
+  const int64_t row = blockIdx.x;  // seq * num_heads + head
+  const int s = static_cast<int>(row / num_heads);
+  const int L = context_lens[s];
+  const int n = (L + partition - 1) / partition;
+  if (n <= 1) return;
+  const int64_t row0 = row * num_parts;
+  const float2* ml = reinterpret_cast<const float2*>(ws.ml) + row0;
+  float M = -INFINITY;
+  for (int p = lane; p < n; p += 64) M = fmaxf(M, ml[p].x);
+  M = pa::wave_max_u(M);
+  const vec_t* po = reinterpret_cast<const vec_t*>(ws.o + row0 * D) + lane;
+  vec_t acc = {};
+  float wsum = 0.f;
+  for (int p0 = 0; p0 < n; p0 += 64) {
+    float w = 0.f;
+    if (p0 + lane < n) {
+      const float2 v = ml[p0 + lane];
+      w = v.y * pa::fast_exp2(v.x - M);
+    }
+    wsum += w;
+    const int cnt = min(64, n - p0);
+    const vec_t* pj = po + p0 * 64;
+    int j = 0;
+    for (; j + 4 <= cnt; j += 4) {  // four partitions' loads in flight
+      const vec_t o0 = pj[j * 64], o1 = pj[(j + 1) * 64], o2 = pj[(j + 2) * 64],
+                  o3 = pj[(j + 3) * 64];
+      acc += pa::readlane_f(w, j) * o0;
+      acc += pa::readlane_f(w, j + 1) * o1;
+      acc += pa::readlane_f(w, j + 2) * o2;
+      acc += pa::readlane_f(w, j + 3) * o3;
+    }
+    for (; j < cnt; ++j) acc += pa::readlane_f(w, j) * pj[j * 64];
+  }
+  const float inv = 1.f / pa::wave_sum_u(wsum);
+  T* dst = out + row * D + lane * PER;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) store_out<T>(dst + i, acc[i] * inv);
+}
+
 constexpr size_t kAlign = 256;
+#ifndef PA_GROUP_WAVES8
+#define PA_GROUP_WAVES8 4
+#endif
+constexpr int kGroupWaves8 = PA_GROUP_WAVES8;  // waves per workgroup for 8-head groups
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -448,13 +731,21 @@ int launch_decode(void* out, const void* q, const void* kc, const void* vc, cons
     p.ml = reinterpret_cast<float*>(base);
   }
   const int64_t grid = static_cast<int64_t>(parts) * KVH * B;
-  hipLaunchKernelGGL((decode_kernel<T, D, G, PVB>), dim3(static_cast<uint32_t>(grid)), dim3(64), 0,
-                     st, static_cast<T*>(out), p, static_cast<const T*>(q),
-                     static_cast<const T*>(kc), static_cast<const T*>(vc), bt, max_blocks, lens, B,
-                     H, KVH, parts, partition, scale_log2);
+  if constexpr (sizeof(T) == 2 && D == 128 && (G == 4 || G == 8)) {
+    constexpr int W = G == 8 ? kGroupWaves8 : 4;
+    hipLaunchKernelGGL((decode_group_kernel<G / W, W>), dim3(static_cast<uint32_t>(grid)), dim3(W * 64),
+                       0, st, static_cast<uint16_t*>(out), p, static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(kc), static_cast<const uint16_t*>(vc), bt,
+                       max_blocks, lens, B, H, KVH, parts, partition, scale_log2);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<T, D, G, PVB>), dim3(static_cast<uint32_t>(grid)), dim3(64),
+                       0, st, static_cast<T*>(out), p, static_cast<const T*>(q),
+                       static_cast<const T*>(kc), static_cast<const T*>(vc), bt, max_blocks, lens,
+                       B, H, KVH, parts, partition, scale_log2);
+  }
   if (parts > 1)
-    hipLaunchKernelGGL((decode_merge_kernel<T, D, G>), dim3(static_cast<uint32_t>(B) * KVH),
-                       dim3(64), 0, st, static_cast<T*>(out), p, lens, B, H, KVH, parts, partition);
+    hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(static_cast<uint32_t>(B) * H), dim3(64),
+                       0, st, static_cast<T*>(out), p, lens, H, parts, partition);
   return pa_launch_status();
 }
 

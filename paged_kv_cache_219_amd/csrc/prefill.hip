@@ -31,19 +31,21 @@
 // XCD at the same time: its K/V pages come from HBM once and are served to the
 // other q-tiles from that XCD's L2.
 
-#include "pa_device.h"
+#include "page_ring.h"
 
 namespace {
 
-constexpr int kBS = 16;
-constexpr int kD = 128;
+using pa::ring::kBS;
+using pa::ring::kD;
+using pa::ring::kPageElems;
+using pa::ring::kPages;
+using pa::ring::kRing;
+using pa::ring::kStep;
+using pa::ring::StepBuf;
+using pa::ring::vhalf;
 constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 32;
 constexpr int kRowsPerWG = kWaves * kRowsPerWave;
-constexpr int kPages = 2;             // pages per step
-constexpr int kRing = 4;              // LDS step buffers (loads run kRing-1 steps ahead)
-constexpr int kStep = kPages * kBS;   // tokens per step
-constexpr int kPageElems = kBS * kD;  // elements of one (block, head) page
 constexpr uint32_t kXcds = 8;
 constexpr float kLazyRescale = 8.f;   // log2 units
 
@@ -55,37 +57,6 @@ __device__ __forceinline__ pa::f32x16_t mfma32(uint4 a, uint4 b, pa::f32x16_t c)
 }
 
 __device__ __forceinline__ float swap32_max(float v) { return fmaxf(v, __shfl_xor(v, 32, 64)); }
-
-// LDS layout of one step buffer, in 16-byte units:
-//   K: [page][chunk 16][token 16]  -- the global page layout
-//   V: [page][dim 128][2 halves of 8 tokens], the two halves of each dim row
-//      swapped when (dim / 8) is odd, so the V^T operand reads (32 dims x 8
-//      bytes) hit distinct bank pairs.
-// Steps are copied with direct-to-LDS loads (lane i of a wave instruction
-// lands at base + 16 i), each lane fetching the global unit that belongs at its
-// LDS position.
-struct StepBuf {
-  uint4 k[kPages * 256];
-  uint4 v[kPages * 256];
-};
-
-__device__ __forceinline__ int vhalf(int d, int half) { return half ^ ((d >> 3) & 1); }
-
-// 16-byte direct-to-LDS load: lane i's bytes land at LDS byte address
-// lds_base + 16 i.  Issued through asm so the compiler does not pair every
-// later LDS read with a wait for all outstanding copies; the kernel waits for
-// them explicitly (vmcnt) before the barrier that publishes a step.
-__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(lds_base)
-               : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
-}
 
 // grid (ceil(max_query_len / 128) * num_heads * num_seqs rounded up to 8), 256 threads.
 __global__ __launch_bounds__(256, 2) void prefill_chunk_kernel(
@@ -145,27 +116,12 @@ __global__ __launch_bounds__(256, 2) void prefill_chunk_kernel(
   const int64_t blk_stride = static_cast<int64_t>(num_kv_heads) * kPageElems;
   const int64_t head_off = static_cast<int64_t>(g) * kPageElems;
 
-  // Each wave copies 2 x 1 KB of K and 2 x 1 KB of V per step (the step is
-  // 2 pages = 8 KB of each).  Unit u = 128 * wave + 64 * i + lane.  Pages past
-  // the last needed token load logical block 0 instead (always valid): their
-  // scores are masked, and their values must just be finite.
+  // Pages past the last needed token load logical block 0 instead (always
+  // valid): their scores are masked, and their values must just be finite.
   auto issue = [&](int step) {
-    StepBuf& B = buf[step % kRing];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int u0 = 128 * wave + 64 * i;  // wave-uniform base unit
-      const int u = u0 + lane;
-      const int page = u0 >> 8;            // a 64-unit run never crosses a page
-      const int lb = step * kPages + page;
-      const int phys = bt_row[lb * kBS <= wg_last ? lb : 0];
-      const uint16_t* kp = kc + phys * blk_stride + head_off;
-      const uint16_t* vp = vc + phys * blk_stride + head_off;
-      const int pos = u & 255;
-      const int d = pos >> 1;
-      lds_dma16(kp + pos * 8, __builtin_amdgcn_readfirstlane(lds_addr(&B.k[u0])));
-      lds_dma16(vp + (d * 2 + vhalf(d, pos & 1)) * 8,
-                __builtin_amdgcn_readfirstlane(lds_addr(&B.v[u0])));
-    }
+    const int lb = step * kPages + (wave >> 1);
+    pa::ring::issue_step(buf[step % kRing], kc, vc, bt_row[lb * kBS <= wg_last ? lb : 0],
+                         blk_stride, head_off, wave, lane);
   };
   // Values of tokens at or past L in the step's last page: zero them in LDS
   // (the cache may hold NaN there, and 0 * NaN would reach every query).
@@ -203,12 +159,7 @@ __global__ __launch_bounds__(256, 2) void prefill_chunk_kernel(
     const StepBuf& B = buf[step % kRing];
     // wait for this wave's copies of this step (later steps may stay in
     // flight), then for everyone's
-    const int ahead = min(kRing - 2, nsteps - 1 - step);
-    if (ahead >= 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else if (ahead == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+    pa::ring::wait_step(min(kRing - 2, nsteps - 1 - step));
     const int t0 = step * kStep;
     if (t0 + kStep > L) {  // the step holding the sequence's last token
       zero_tail(step);
@@ -226,7 +177,8 @@ __global__ __launch_bounds__(256, 2) void prefill_chunk_kernel(
       const int m = lane & 31;  // token row of the K operand
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        const uint4 a0 = B.k[((m >> 4) * 16 + 2 * kk + hh) * 16 + (m & 15)];
+        const int c = 2 * kk + hh;
+        const uint4 a0 = B.k[((m >> 4) * 16 + c) * 16 + pa::ring::kslot(c, m & 15)];
         sa = mfma32(a0, qreg[kk], sa);
       }
       // ---- online softmax over this lane's 16 tokens (query qn).  Token of

@@ -103,12 +103,12 @@ def test_decode_configs_scaled(name, scale_down):
     say(f"  max abs {mx:.2e} rel L2 {rel:.2e}")
 
 
-EDGE_LENS = [1, 2, 15, 16, 17, 63, 64, 65, 127, 128, 129, 511, 512, 513, 1000]
+EDGE_LENS = [1, 2, 15, 16, 17, 31, 32, 33, 48, 63, 64, 65, 127, 128, 129, 511, 512, 513, 1000]
 
 
 @pytest.mark.parametrize("dtype,H,KVH,D", [("bf16", 4, 4, 128), ("bf16", 16, 2, 128),
                                            ("bf16", 8, 2, 64), ("f32", 4, 4, 64),
-                                           ("bf16", 4, 2, 128), ("f32", 8, 1, 64),
+                                           ("bf16", 4, 2, 128), ("bf16", 8, 2, 128), ("f32", 8, 1, 64),
                                            ("f32", 2, 2, 128)])
 @pytest.mark.parametrize("partition", [0, 64, 192])
 def test_decode_edge_lengths_and_partitions(dtype, H, KVH, D, partition):
