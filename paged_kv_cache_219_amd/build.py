@@ -33,11 +33,18 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
           "-munsafe-fp-atomics"]
 
 
+# Per-source extras.  The prefill kernel never lets a NaN reach arithmetic
+# that matters (masked scores are replaced by -inf with a select, tail values
+# are zeroed bitwise), so it is built assuming no NaN operands: fmax then needs
+# no canonicalising instruction per operand.
+EXTRA = {"prefill.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str) -> str:
     path = os.path.join(CSRC, src)
     obj = os.path.join(BUILD, src + ".o")
     if src.endswith(".hip"):
-        cmd = [HIPCC, "-x", "hip", *COMMON, *DEVICE, "-c", path, "-o", obj]
+        cmd = [HIPCC, "-x", "hip", *COMMON, *DEVICE, *EXTRA.get(src, []), "-c", path, "-o", obj]
     else:
         cmd = [HIPCC, *COMMON, "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

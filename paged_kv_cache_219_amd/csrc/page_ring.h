@@ -61,7 +61,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // 64 units (1 KB) of keys and the same of values, all within one page.
 template <int W>
 __device__ __forceinline__ int page_of(int wave) {
-  static_assert(W == 4 || W == 8, "4 or 8 waves per workgroup");
+  static_assert(W == 2 || W == 4 || W == 8, "2, 4 or 8 waves per workgroup");
   return wave / (W / 2);
 }
 
@@ -95,10 +95,12 @@ __device__ __forceinline__ void wait_step(int ahead) {
   static_assert(R >= 2 && R <= 4, "ring of 2 to 4 steps");
   constexpr int kPer = 16 / W;
   if (R == 4 && ahead >= 2) {
-    if (kPer == 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    if (kPer == 8) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if (kPer == 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
   } else if (ahead >= 1) {
-    if (kPer == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    if (kPer == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if (kPer == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
   } else {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

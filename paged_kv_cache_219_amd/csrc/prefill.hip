@@ -43,9 +43,6 @@ using pa::ring::kRing;
 using pa::ring::kStep;
 using pa::ring::StepBuf;
 using pa::ring::vhalf;
-constexpr int kWaves = 4;
-constexpr int kRowsPerWave = 32;
-constexpr int kRowsPerWG = kWaves * kRowsPerWave;
 constexpr uint32_t kXcds = 8;
 constexpr float kLazyRescale = 8.f;   // log2 units
 
@@ -58,26 +55,55 @@ __device__ __forceinline__ pa::f32x16_t mfma32(uint4 a, uint4 b, pa::f32x16_t c)
 
 __device__ __forceinline__ float swap32_max(float v) { return fmaxf(v, __shfl_xor(v, 32, 64)); }
 
-// grid (ceil(max_query_len / 128) * num_heads * num_seqs rounded up to 8), 256 threads.
-__global__ __launch_bounds__(256, 2) void prefill_chunk_kernel(
+// grid (ceil(max_query_len / rows per workgroup) * num_heads * num_seqs rounded
+// up to 8), W * 64 threads.  W waves per workgroup, NB blocks of 32 query rows
+// per wave (every K and V operand read from LDS feeds NB matrix products).
+template <int W, int NB>
+__global__ __launch_bounds__(W * 64, NB == 1 ? 2 : 1) void prefill_chunk_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ block_tables, int32_t max_blocks,
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ context_lens, int32_t num_seqs,
     int32_t num_heads, int32_t num_kv_heads, int32_t num_qtiles, float scale_log2) {
+  constexpr int kRowsPerWave = 32 * NB;
+  constexpr int kRowsPerWG = W * kRowsPerWave;
+  constexpr int kMaxIds = 2048;  // block ids staged in LDS (contexts up to 32768 tokens)
   __shared__ StepBuf buf[kRing];
-
-  // XCD-aware order: logical = (seq, head, q-tile) with q-tile fastest, and XCD
-  // x runs the x-th contiguous slice, so a (seq, head)'s q-tiles share an L2.
-  const uint32_t per_xcd = gridDim.x / kXcds;
-  const uint32_t li = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  const int qt = num_qtiles - 1 - static_cast<int>(li % num_qtiles);  // long q-tiles first
-  const uint32_t sh = li / num_qtiles;
-  const int h = static_cast<int>(sh % static_cast<uint32_t>(num_heads));
-  const int s = static_cast<int>(sh / static_cast<uint32_t>(num_heads));
-  if (s >= num_seqs) return;  // grid padding (whole workgroup)
+  __shared__ int ids_lds[kMaxIds];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+
+  // Order of work.  A unit is one (sequence, head); its q-tiles share the
+  // unit's K/V pages.  Units run longest first (when there are at most 64
+  // sequences, every workgroup ranks them by their number of steps; heads of
+  // a sequence are equal), so the longest workgroups do not start last and
+  // leave the chip idle behind them.  Unit u runs on XCD u % 8 and its q-tiles
+  // are consecutive there (dispatch sends workgroup b to XCD b % 8), so they
+  // are in flight together and read the unit's pages from HBM once, through
+  // that XCD's L2.
+  const uint32_t xcd = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
+  const uint32_t u = (k / num_qtiles) * kXcds + xcd;
+  const int qt = num_qtiles - 1 - static_cast<int>(k % num_qtiles);  // long q-tiles first
+  if (u >= static_cast<uint32_t>(num_seqs) * num_heads) return;  // grid padding
+  const int h = static_cast<int>(u % static_cast<uint32_t>(num_heads));
+  const int rank = static_cast<int>(u / static_cast<uint32_t>(num_heads));
+  int s = rank;
+  if (num_seqs <= 64) {
+    int work = -1;
+    if (lane < num_seqs) {
+      const int Li = context_lens[lane], nqi = qsl[lane + 1] - qsl[lane];
+      work = 0;
+      for (int t = 0; t < num_qtiles && t * kRowsPerWG < nqi; ++t)
+        work += (Li - nqi + min((t + 1) * kRowsPerWG, nqi) - 1) / kStep + 1;
+    }
+    int my_rank = 0;
+    for (int j = 0; j < num_seqs; ++j) {
+      const int wj = __builtin_amdgcn_readlane(work, j);
+      my_rank += (wj > work) || (wj == work && j < lane);
+    }
+    s = __builtin_ctzll(__ballot(lane < num_seqs && my_rank == rank));
+  }
+
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = h / (num_heads / num_kv_heads);
   const int q0 = qsl[s];
@@ -91,45 +117,60 @@ __global__ __launch_bounds__(256, 2) void prefill_chunk_kernel(
 
   const int row0 = wg_row0 + wave * kRowsPerWave;
   const bool wave_active = row0 < n_q;
-  const int qn = lane & 31;   // this lane's query column
+  const int qn = lane & 31;   // this lane's query column within a block
   const int hh = lane >> 5;   // which half of the accumulator rows
-  const int my_row = min(row0 + qn, n_q - 1);
-  const int my_pos = first_pos + my_row;
   const int wave_last = first_pos + min(row0 + kRowsPerWave, n_q) - 1;
   const int wave_first = first_pos + row0;
+  int my_pos[NB];
 
-  // Q^T operand: lane (qn, hh) holds dims 16*kk + 8*hh .. +7 of its query row.
-  uint4 qreg[8];
-  {
+  // Q^T operands: lane (qn, hh) holds dims 16*kk + 8*hh .. +7 of its query
+  // row in each block.
+  uint4 qreg[NB][8];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int my_row = min(row0 + 32 * b + qn, n_q - 1);
+    my_pos[b] = first_pos + my_row;
     const uint16_t* qrow = q + (static_cast<int64_t>(q0 + my_row) * num_heads + h) * kD + 8 * hh;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qreg[kk] = *reinterpret_cast<const uint4*>(qrow + 16 * kk);
-    // Consume the query registers here: otherwise their load waits land in
-    // the step loop, where (loads retiring in order) they would also drain
-    // every step copy in flight.
+    for (int kk = 0; kk < 8; ++kk) qreg[b][kk] = *reinterpret_cast<const uint4*>(qrow + 16 * kk);
+  }
+  // Consume the query registers here: otherwise their load waits land in the
+  // step loop, where (loads retiring in order) they would also drain every
+  // step copy in flight.
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
-      asm volatile("" : "+v"(qreg[kk].x), "+v"(qreg[kk].y), "+v"(qreg[kk].z), "+v"(qreg[kk].w));
-  }
+      asm volatile("" : "+v"(qreg[b][kk].x), "+v"(qreg[b][kk].y), "+v"(qreg[b][kk].z),
+                   "+v"(qreg[b][kk].w));
 
   const int32_t* bt_row = block_tables + static_cast<int64_t>(s) * max_blocks;
   const int64_t blk_stride = static_cast<int64_t>(num_kv_heads) * kPageElems;
   const int64_t head_off = static_cast<int64_t>(g) * kPageElems;
 
+  // The workgroup's block ids go to LDS once, so issuing a step's copies
+  // waits on an LDS read rather than on a scalar-cache miss.
+  const int npages = wg_last / kBS + 1;
+  const bool ids_staged = npages <= kMaxIds;
+  if (ids_staged)
+    for (int i = tid; i < npages; i += W * 64) ids_lds[i] = bt_row[i];
+  __syncthreads();
+
   // Pages past the last needed token load logical block 0 instead (always
   // valid): their scores are masked, and their values must just be finite.
   auto issue = [&](int step) {
-    const int lb = step * kPages + (wave >> 1);
-    pa::ring::issue_step(buf[step % kRing], kc, vc, bt_row[lb * kBS <= wg_last ? lb : 0],
-                         blk_stride, head_off, wave, lane);
+    int lb = step * kPages + pa::ring::page_of<W>(wave);
+    if (lb >= npages) lb = 0;
+    const int phys = ids_staged ? __builtin_amdgcn_readfirstlane(ids_lds[lb]) : bt_row[lb];
+    pa::ring::issue_step<W>(buf[step % kRing], kc, vc, phys, blk_stride, head_off, wave, lane);
   };
   // Values of tokens at or past L in the step's last page: zero them in LDS
   // (the cache may hold NaN there, and 0 * NaN would reach every query).
   auto zero_tail = [&](int step) {
     StepBuf& B = buf[step % kRing];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int row = tid + 256 * r;      // (page, dim) row, 2 units each
+    for (int r = 0; r < 512 / (W * 64); ++r) {
+      const int row = tid + W * 64 * r;   // (page, dim) row, 2 units each
       const int page = row >> 7, d = row & 127;
       const int tok0 = (step * kPages + page) * kBS;
       uint4* vr = &B.v[page * 256 + d * 2];
@@ -148,20 +189,106 @@ __global__ __launch_bounds__(256, 2) void prefill_chunk_kernel(
     }
   };
 
-  pa::f32x16_t o[4];
+  pa::f32x16_t o[NB][4];
+  float m_run[NB], l_run[NB], neg_m[NB];  // neg_m: -m_run, or 0 while m_run is -inf
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = pa::f32x16_t{};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int b = 0; b < NB; ++b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[b][i] = pa::f32x16_t{};
+    m_run[b] = -INFINITY;
+    l_run[b] = 0.f;
+    neg_m[b] = 0.f;
+  }
+
+  // Row m of the K operand (and of S^T) holds token krow(m) of the step: m
+  // with bits 2 and 3 swapped.  Then the 16 accumulator rows of lane (q, hh)
+  // -- rows 8*(j/4) + 4*hh + j%4 -- are tokens 16*(j/8) + 8*hh + j%8, i.e.
+  // 8 consecutive tokens of each page, exactly the k-slots 8*hh..8*hh+7 of
+  // the PV product's P^T operand; so the matching V^T operand is one 16-byte
+  // half row of the d-major value page.
+  const int m_row = lane & 31;
+  const int ktok = (m_row & 0x13) | ((m_row & 4) << 1) | ((m_row & 8) >> 1);
+
+  auto step_compute = [&](int step) {
+    const StepBuf& B = buf[step % kRing];
+    const int t0 = step * kStep;
+    // ---- S^T = K Q^T, each K operand feeding every block
+    pa::f32x16_t sa[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) sa[b] = pa::f32x16_t{};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int c = 2 * kk + hh;
+      const uint4 a0 = B.k[((ktok >> 4) * 16 + c) * 16 + pa::ring::kslot(c, ktok & 15)];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) sa[b] = mfma32(a0, qreg[b][kk], sa[b]);
+    }
+    // ---- online softmax per block: lane (qn, hh) element j is token
+    // t0 + 16*(j/8) + 8*hh + j%8 of query row 32*b + qn
+    uint4 pb[NB][kPages];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      float x[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) x[j] = sa[b][j];
+      if (t0 + kStep - 1 > wave_first + 32 * b || t0 + kStep > L) {  // diagonal or tail step
+        const int lim = min(my_pos[b], L - 1) - t0 - 8 * hh;         // keep offsets <= lim
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int off = 16 * (j >> 3) + (j & 7);
+          if (off > lim) x[j] = -INFINITY;
+        }
+      }
+      float mx = fmaxf(x[0], x[1]);
+#pragma unroll
+      for (int j = 2; j < 16; j += 2) mx = fmaxf(mx, fmaxf(x[j], x[j + 1]));
+      // Lazy rescale, wave-uniform: only when some query's score exceeds its
+      // reference by more than 2^8 (scale > 0: max commutes with it).  Only
+      // then are the two halves of each query column combined.
+      if (__any(mx * scale_log2 > m_run[b] + kLazyRescale)) {
+        const float m_new = fmaxf(m_run[b], swap32_max(mx) * scale_log2);
+        const float alpha = pa::fast_exp2(m_run[b] - m_new);
+        l_run[b] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[b][i] *= alpha;
+        m_run[b] = m_new;
+        neg_m[b] = m_new == -INFINITY ? 0.f : -m_new;
+      }
+      uint32_t pw[8];
+      float ls = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) {
+        const float p0 = pa::fast_exp2(fmaf(x[j], scale_log2, neg_m[b]));
+        const float p1 = pa::fast_exp2(fmaf(x[j + 1], scale_log2, neg_m[b]));
+        ls += p0 + p1;
+        pw[j >> 1] = pa::pack_bf16x2(p0, p1);
+      }
+      l_run[b] += ls;
+      // P^T operands, one per page: elements 8*pg .. 8*pg+7 are tokens
+      // 8*hh .. 8*hh+7 of page pg.
+#pragma unroll
+      for (int pg = 0; pg < kPages; ++pg)
+        pb[b][pg] = make_uint4(pw[4 * pg], pw[4 * pg + 1], pw[4 * pg + 2], pw[4 * pg + 3]);
+    }
+    // ---- O^T += V^T P^T, each V operand feeding every block
+#pragma unroll
+    for (int pg = 0; pg < kPages; ++pg) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int d = dt * 32 + (lane & 31);
+        const uint4 va = B.v[pg * 256 + d * 2 + vhalf(d, hh)];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) o[b][dt] = mfma32(va, pb[b][pg], o[b][dt]);
+      }
+    }
+  };
 
   for (int st = 0; st < kRing - 1 && st < nsteps; ++st) issue(st);
-
   for (int step = 0; step < nsteps; ++step) {
-    const StepBuf& B = buf[step % kRing];
     // wait for this wave's copies of this step (later steps may stay in
     // flight), then for everyone's
-    pa::ring::wait_step(min(kRing - 2, nsteps - 1 - step));
-    const int t0 = step * kStep;
-    if (t0 + kStep > L) {  // the step holding the sequence's last token
+    pa::ring::wait_step<kRing, W>(min(kRing - 2, nsteps - 1 - step));
+    if (step * kStep + kStep > L) {  // the step holding the sequence's last token
       zero_tail(step);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
@@ -170,89 +297,39 @@ __global__ __launch_bounds__(256, 2) void prefill_chunk_kernel(
     // the buffer written next was last read in the previous step, which every
     // wave has finished (barrier above)
     if (step + kRing - 1 < nsteps) issue(step + kRing - 1);
-
-    if (wave_active && t0 <= wave_last) {
-      // ---- S^T = K Q^T
-      pa::f32x16_t sa = pa::f32x16_t{};
-      const int m = lane & 31;  // token row of the K operand
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const int c = 2 * kk + hh;
-        const uint4 a0 = B.k[((m >> 4) * 16 + c) * 16 + pa::ring::kslot(c, m & 15)];
-        sa = mfma32(a0, qreg[kk], sa);
-      }
-      // ---- online softmax over this lane's 16 tokens (query qn).  Token of
-      // element j: t0 + 8*(j/4) + 4*hh + j%4.
-      float x[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) x[j] = sa[j];
-      if (t0 + kStep - 1 > wave_first || t0 + kStep > L) {  // diagonal or tail step
-        const int lim = min(my_pos, L - 1) - t0 - 4 * hh;   // keep offsets <= lim
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int off = 8 * (j >> 2) + (j & 3);
-          if (off > lim) x[j] = -INFINITY;
-        }
-      }
-      float mx = fmaxf(x[0], x[1]);
-#pragma unroll
-      for (int j = 2; j < 16; j += 2) mx = fmaxf(mx, fmaxf(x[j], x[j + 1]));
-      mx = swap32_max(mx) * scale_log2;  // scale > 0: max commutes with it
-      // Lazy rescale, wave-uniform: only when some query's max grew by > 2^8.
-      if (__any(mx > m_run + kLazyRescale)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = pa::fast_exp2(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] *= alpha;
-        m_run = m_new;
-      }
-      const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
-      uint32_t pw[8];
-      float ls = 0.f;
-#pragma unroll
-      for (int j = 0; j < 16; j += 2) {
-        const float p0 = pa::fast_exp2(fmaf(x[j], scale_log2, neg_m));
-        const float p1 = pa::fast_exp2(fmaf(x[j + 1], scale_log2, neg_m));
-        ls += p0 + p1;
-        pw[j >> 1] = pa::pack_bf16x2(p0, p1);
-      }
-      l_run += ls;
-      // P^T operands, one per page: page pg's 16 tokens are the lane's
-      // elements 8*pg .. 8*pg+7 (tokens 4hh..+3 and 8+4hh..+3 of that page).
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int pg = 0; pg < kPages; ++pg) {
-        const uint4 pb = make_uint4(pw[4 * pg], pw[4 * pg + 1], pw[4 * pg + 2], pw[4 * pg + 3]);
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const int d = dt * 32 + (lane & 31);
-          // tokens 4hh..+3 (half 0, byte 8*hh) and 8+4hh..+3 (half 1, byte 8*hh)
-          const uint2* r0 = reinterpret_cast<const uint2*>(&B.v[pg * 256 + d * 2 + vhalf(d, 0)]);
-          const uint2* r1 = reinterpret_cast<const uint2*>(&B.v[pg * 256 + d * 2 + vhalf(d, 1)]);
-          const uint2 lo = r0[hh], hi = r1[hh];
-          o[dt] = mfma32(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, o[dt]);
-        }
-      }
-    }
+    if (wave_active && step * kStep <= wave_last) step_compute(step);
   }
 
   if (!wave_active) return;
-  const float lt = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (row0 + qn < n_q) {
-    uint16_t* orow = out + (static_cast<int64_t>(q0 + row0 + qn) * num_heads + h) * kD;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+  for (int b = 0; b < NB; ++b) {
+    const float lt = l_run[b] + __shfl_xor(l_run[b], 32, 64);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const int row = row0 + 32 * b + qn;
+    if (row < n_q) {
+      uint16_t* orow = out + (static_cast<int64_t>(q0 + row) * num_heads + h) * kD;
 #pragma unroll
-      for (int jg = 0; jg < 4; ++jg) {
-        uint2 w;
-        w.x = pa::pack_bf16x2(o[dt][4 * jg] * inv, o[dt][4 * jg + 1] * inv);
-        w.y = pa::pack_bf16x2(o[dt][4 * jg + 2] * inv, o[dt][4 * jg + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + dt * 32 + 8 * jg + 4 * hh) = w;
-      }
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          uint2 w;
+          w.x = pa::pack_bf16x2(o[b][dt][4 * jg] * inv, o[b][dt][4 * jg + 1] * inv);
+          w.y = pa::pack_bf16x2(o[b][dt][4 * jg + 2] * inv, o[b][dt][4 * jg + 3] * inv);
+          *reinterpret_cast<uint2*>(orow + dt * 32 + 8 * jg + 4 * hh) = w;
+        }
+    }
   }
 }
+
+#ifndef PA_PREFILL_WAVES
+#define PA_PREFILL_WAVES 4
+#endif
+#ifndef PA_PREFILL_BLOCKS
+#define PA_PREFILL_BLOCKS 1
+#endif
+constexpr int kWaves = PA_PREFILL_WAVES;
+constexpr int kBlocks = PA_PREFILL_BLOCKS;
+constexpr int kRowsPerWG = kWaves * 32 * kBlocks;
 
 }  // namespace
 
@@ -276,11 +353,12 @@ extern "C" int pa_prefill_chunk(void* out, const void* q, const void* k_cache,
        reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache)) & 15)
     return PA_ERR_INVALID_ARG;
   const int64_t qtiles = (static_cast<int64_t>(max_query_len) + kRowsPerWG - 1) / kRowsPerWG;
-  const int64_t wgs = qtiles * num_heads * num_seqs;
-  const int64_t grid = (wgs + kXcds - 1) / kXcds * kXcds;
+  const int64_t units = static_cast<int64_t>(num_heads) * num_seqs;
+  const int64_t grid = (units + kXcds - 1) / kXcds * kXcds * qtiles;
   if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
   const float sl2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
-  hipLaunchKernelGGL(prefill_chunk_kernel, dim3(static_cast<uint32_t>(grid)), dim3(256), 0,
+  hipLaunchKernelGGL((prefill_chunk_kernel<kWaves, kBlocks>), dim3(static_cast<uint32_t>(grid)),
+                     dim3(kWaves * 64), 0,
                      static_cast<hipStream_t>(stream), static_cast<uint16_t*>(out),
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
                      static_cast<const uint16_t*>(v_cache), block_tables, max_blocks_per_seq,
