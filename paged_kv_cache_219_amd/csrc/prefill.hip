@@ -66,9 +66,7 @@ __global__ __launch_bounds__(W * 64, NB == 1 ? 2 : 1) void prefill_chunk_kernel(
     int32_t num_heads, int32_t num_kv_heads, int32_t num_qtiles, float scale_log2) {
   constexpr int kRowsPerWave = 32 * NB;
   constexpr int kRowsPerWG = W * kRowsPerWave;
-  constexpr int kMaxIds = 2048;  // block ids staged in LDS (contexts up to 32768 tokens)
   __shared__ StepBuf buf[kRing];
-  __shared__ int ids_lds[kMaxIds];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -148,21 +146,12 @@ __global__ __launch_bounds__(W * 64, NB == 1 ? 2 : 1) void prefill_chunk_kernel(
   const int64_t blk_stride = static_cast<int64_t>(num_kv_heads) * kPageElems;
   const int64_t head_off = static_cast<int64_t>(g) * kPageElems;
 
-  // The workgroup's block ids go to LDS once, so issuing a step's copies
-  // waits on an LDS read rather than on a scalar-cache miss.
-  const int npages = wg_last / kBS + 1;
-  const bool ids_staged = npages <= kMaxIds;
-  if (ids_staged)
-    for (int i = tid; i < npages; i += W * 64) ids_lds[i] = bt_row[i];
-  __syncthreads();
-
   // Pages past the last needed token load logical block 0 instead (always
   // valid): their scores are masked, and their values must just be finite.
   auto issue = [&](int step) {
-    int lb = step * kPages + pa::ring::page_of<W>(wave);
-    if (lb >= npages) lb = 0;
-    const int phys = ids_staged ? __builtin_amdgcn_readfirstlane(ids_lds[lb]) : bt_row[lb];
-    pa::ring::issue_step<W>(buf[step % kRing], kc, vc, phys, blk_stride, head_off, wave, lane);
+    const int lb = step * kPages + pa::ring::page_of<W>(wave);
+    pa::ring::issue_step<W>(buf[step % kRing], kc, vc, bt_row[lb * kBS <= wg_last ? lb : 0],
+                            blk_stride, head_off, wave, lane);
   };
   // Values of tokens at or past L in the step's last page: zero them in LDS
   // (the cache may hold NaN there, and 0 * NaN would reach every query).
