@@ -269,6 +269,30 @@ def cpu_baseline(budget_s: float = 10.0, max_passes: int = 8):
             "seq_tokens_per_s": B * passes / elapsed}
 
 
+def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
+    """A plain device-to-device copy of ``nbytes`` (torch's copy_, a runtime
+    blit): its rate is the achievable streaming read+write bandwidth, and
+    under rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE per dispatch calibrate
+    the counters against a known byte count."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "ms": ms,
+            "copy_GBs": 2 * nbytes / (ms * 1e-3) / 1e9}
+
+
 # ---------------------------------------------------------------------------
 # rocprofv3 summaries (profiles/) and the measured HBM traffic they carry.
 # The counters come from separate profiler runs of this same script (a

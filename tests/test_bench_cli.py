@@ -1,0 +1,48 @@
+"""CPU checks of bench.py's command line and helpers (no GPU)."""
+
+import csv
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_bench_defines_every_step_of_main():
+    for name in ("bench_decode", "bench_prefill", "cpu_baseline", "copy_calibration",
+                 "measured_traffic", "summarize_stats", "summarize_traffic", "main"):
+        assert callable(getattr(bench, name)), name
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_traffic_summary_scales_by_the_copy_calibration(tmp_path):
+    cols = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    rows = {
+        "FETCH_SIZE": [("1", "__amd_rocclr_copyBuffer", "524288"),
+                       ("2", "void decode_kernel<x>(int)", "1000"),
+                       ("3", "void decode_merge_kernel<x>(int)", "10")],
+        "WRITE_SIZE": [("1", "__amd_rocclr_copyBuffer", "1048576"),
+                       ("2", "void decode_kernel<x>(int)", "4"),
+                       ("3", "void decode_merge_kernel<x>(int)", "2")],
+    }
+    paths = []
+    for ctr, rs in rows.items():
+        p = tmp_path / f"{ctr}.csv"
+        with open(p, "w", newline="") as f:
+            w = csv.writer(f)
+            w.writerow(cols)
+            for d, k, v in rs:
+                w.writerow([d, k, ctr, v])
+        paths.append(str(p))
+    text = bench.summarize_traffic(*paths)
+    line = [l for l in text.splitlines() if l.startswith("@traffic_bytes_per_call")][0]
+    # fetch counts half the bytes (factor 2), writes count them all (factor 1)
+    assert float(line.split(":")[1]) == (1000 + 10) * 1024 * 2 + (4 + 2) * 1024
