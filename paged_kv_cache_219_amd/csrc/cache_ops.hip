@@ -15,9 +15,14 @@
 
 namespace {
 
-// One wave per (token, kv head).  Lanes copy the key row as 16-byte chunks
-// (each chunk is one x-packed group of the key layout) and the value row
-// element by element into its d-major page.
+// One wave per (group of X consecutive tokens, kv head), X = 16 / element
+// size: the number of tokens in one 16-byte unit of the d-major value page.
+//  * keys: the X tokens' rows as 16-byte chunks, each to its x-packed place;
+//  * values: when the group's slots are X consecutive slots starting at a
+//    multiple of X (the common case when a chunk of a sequence is written),
+//    each lane gathers one dimension of the X tokens and stores it as one
+//    16-byte unit of the page; otherwise each token's values are stored
+//    element by element.
 template <int ESIZE>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const uint8_t* __restrict__ key, const uint8_t* __restrict__ value, uint8_t* __restrict__ kc,
@@ -25,26 +30,63 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     int64_t kstride_bytes, int64_t vstride_bytes, int32_t kvh, int32_t head_dim,
     int32_t block_size) {
   typedef typename std::conditional<ESIZE == 2, uint16_t, uint32_t>::type elem_t;
+  constexpr int X = 16 / ESIZE;
   const int lane = threadIdx.x & 63;
   const int64_t w = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  const int64_t tok = w / kvh;
+  const int64_t grp = w / kvh;
   const int head = static_cast<int>(w % kvh);
-  if (tok >= num_tokens) return;
-  const int64_t slot = slots[tok];
-  if (slot < 0) return;
-  const int64_t blk = slot / block_size;
-  const int off = static_cast<int>(slot % block_size);
+  const int64_t tok0 = grp * X;
+  if (tok0 >= num_tokens) return;
+  const int ntok = static_cast<int>(min(static_cast<int64_t>(X), num_tokens - tok0));
   const int nchunk = head_dim * ESIZE / 16;
-  const uint8_t* ksrc = key + tok * kstride_bytes + static_cast<int64_t>(head) * head_dim * ESIZE;
-  uint8_t* kdst = kc + ((blk * kvh + head) * nchunk * block_size + off) * 16;
-  for (int c = lane; c < nchunk; c += 64) {
-    uint4 v = *reinterpret_cast<const uint4*>(ksrc + c * 16);
-    *reinterpret_cast<uint4*>(kdst + static_cast<int64_t>(c) * block_size * 16) = v;
+
+  // this group's slots, one per lane (lanes >= ntok hold -1)
+  const int64_t my_slot = lane < ntok ? slots[tok0 + lane] : -1;
+
+  // ---- keys
+  for (int u = lane; u < X * nchunk; u += 64) {
+    const int j = u / nchunk, c = u - (u / nchunk) * nchunk;
+    const int64_t slot = __shfl(my_slot, j, 64);
+    if (j < ntok && slot >= 0) {
+      const int64_t blk = slot / block_size;
+      const int off = static_cast<int>(slot % block_size);
+      const uint4 v = *reinterpret_cast<const uint4*>(key + (tok0 + j) * kstride_bytes +
+                                                     static_cast<int64_t>(head) * head_dim * ESIZE +
+                                                     c * 16);
+      *reinterpret_cast<uint4*>(
+          kc + ((((blk * kvh + head) * nchunk + c) * block_size) + off) * 16) = v;
+    }
   }
-  const elem_t* vsrc = reinterpret_cast<const elem_t*>(value + tok * vstride_bytes) +
-                       static_cast<int64_t>(head) * head_dim;
-  elem_t* vdst = reinterpret_cast<elem_t*>(vc) + (blk * kvh + head) * head_dim * block_size + off;
-  for (int d = lane; d < head_dim; d += 64) vdst[static_cast<int64_t>(d) * block_size] = vsrc[d];
+
+  // ---- values
+  const int64_t s0 = __shfl(my_slot, 0, 64);
+  const bool run = ntok == X && s0 >= 0 && s0 % X == 0 &&
+                   __all(lane >= X || my_slot == s0 + lane);
+  if (run) {
+    const int64_t blk = s0 / block_size;
+    const int off = static_cast<int>(s0 % block_size);
+    elem_t* vpage = reinterpret_cast<elem_t*>(vc) + (blk * kvh + head) * head_dim * block_size + off;
+    for (int d = lane; d < head_dim; d += 64) {
+      elem_t e[X];
+#pragma unroll
+      for (int j = 0; j < X; ++j)
+        e[j] = reinterpret_cast<const elem_t*>(value + (tok0 + j) * vstride_bytes)
+            [static_cast<int64_t>(head) * head_dim + d];
+      *reinterpret_cast<uint4*>(vpage + static_cast<int64_t>(d) * block_size) =
+          __builtin_bit_cast(uint4, e);
+    }
+  } else {
+    for (int j = 0; j < ntok; ++j) {
+      const int64_t slot = __shfl(my_slot, j, 64);
+      if (slot < 0) continue;
+      const int64_t blk = slot / block_size;
+      const int off = static_cast<int>(slot % block_size);
+      const elem_t* vsrc = reinterpret_cast<const elem_t*>(value + (tok0 + j) * vstride_bytes) +
+                           static_cast<int64_t>(head) * head_dim;
+      elem_t* vdst = reinterpret_cast<elem_t*>(vc) + (blk * kvh + head) * head_dim * block_size + off;
+      for (int d = lane; d < head_dim; d += 64) vdst[static_cast<int64_t>(d) * block_size] = vsrc[d];
+    }
+  }
 }
 
 // grid (num_pairs, ceil(units / 256)); each thread copies one 16-byte unit of
@@ -80,10 +122,12 @@ extern "C" int pa_reshape_and_cache(const void* key, const void* value, void* k_
   if (key_stride < row || value_stride < row) return PA_ERR_INVALID_ARG;
   if (num_tokens == 0) return PA_OK;
   if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_INVALID_ARG;
-  if ((reinterpret_cast<uintptr_t>(key) | reinterpret_cast<uintptr_t>(k_cache)) & 15)
+  if ((reinterpret_cast<uintptr_t>(key) | reinterpret_cast<uintptr_t>(k_cache) |
+       reinterpret_cast<uintptr_t>(v_cache)) & 15)
     return PA_ERR_INVALID_ARG;
   if (((key_stride * es) & 15) != 0) return PA_ERR_INVALID_ARG;
-  const int64_t waves = static_cast<int64_t>(num_tokens) * num_kv_heads;
+  const int64_t groups = (static_cast<int64_t>(num_tokens) + 16 / es - 1) / (16 / es);
+  const int64_t waves = groups * num_kv_heads;
   const int64_t blocks = (waves + 3) / 4;
   if (blocks > 0x7fffffff) return PA_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);

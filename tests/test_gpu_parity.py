@@ -27,13 +27,39 @@ def _need_gpu():
 
 
 # ------------------------------------------------------------------ cache ops
+def _run_slots(g, nb, T):
+    """Slots as runs of consecutive offsets in shuffled blocks, like a chunk of
+    a sequence written page by page: most runs start at offset 0 (whole
+    16-byte value units), some start mid-page; a few tokens are padding."""
+    blocks = g.permutation(nb)
+    slots, b = [], 0
+    while len(slots) < T:
+        r = g.random()
+        if r < 0.6:
+            start, n = 0, 16                     # a whole page
+        elif r < 0.7:
+            start, n = 8 * int(g.integers(0, 2)), 8  # one aligned 16-byte value unit
+        else:
+            start = int(g.integers(0, 16))
+            n = int(g.integers(1, 17 - start))
+        slots += [int(blocks[b]) * 16 + start + i for i in range(n)]
+        b += 1
+    slots = np.array(slots[:T], np.int64)
+    slots[g.choice(T, size=T // 20, replace=False)] = -1
+    return slots
+
+
+@pytest.mark.parametrize("pattern", ["scattered", "runs"])
 @pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 128)])
-def test_reshape_and_cache_bit_exact_whole_pool(dtype, D):
-    say(f"reshape_and_cache dtype={dtype} D={D}")
+def test_reshape_and_cache_bit_exact_whole_pool(dtype, D, pattern):
+    say(f"reshape_and_cache dtype={dtype} D={D} slots={pattern}")
     g = np.random.default_rng(1)
     nb, kvh, T = 40, 3, 150
-    slots = g.choice(nb * 16, size=T, replace=False).astype(np.int64)
-    slots[::7] = -1  # padding tokens are skipped
+    if pattern == "scattered":
+        slots = g.choice(nb * 16, size=T, replace=False).astype(np.int64)
+        slots[::7] = -1  # padding tokens are skipped
+    else:
+        slots = _run_slots(g, nb, T)
     from synth.draws import _normal
     k = _normal(g, (T, kvh, D), dtype)
     v = _normal(g, (T, kvh, D), dtype)
