@@ -159,6 +159,91 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               size_t workspace_bytes, int32_t dtype, void* stream);
 
 /*
+ * Shared-prefix decode.  Sequences that share the physical blocks of a common
+ * prefix -- the samples of one prompt (the skymod.tech overview on vLLM:
+ * parallel sampling shares the prompt's memory), or requests whose prompts
+ * matched cached blocks (deep-dive page, section "Cơ chế APC", item 2) --
+ * hold the same block ids at the start of their tables.  pa_decode reads
+ * those pages once per sequence; pa_decode_shared_prefix reads them once per
+ * group of up to PA_PREFIX_MAX_MEMBERS neighbouring sequences and attends the
+ * rest of every context as pa_decode does.  The result is pa_decode's (same
+ * softmax, merged with the same log-sum-exp weights) up to fp32 rounding.
+ */
+#define PA_PREFIX_MAX_MEMBERS 8
+
+/*
+ * pa_prefix_plan -- find prefix groups in a batch's block tables (host
+ * memory; no device work).  Greedy in batch order: a group is a run of
+ * consecutive sequences starting at its first member; its prefix is the
+ * leading whole blocks whose ids all members share, in tokens (a multiple of
+ * block_size, at most every member's context).  The next sequence joins while
+ * the group has fewer than max_members (1..PA_PREFIX_MAX_MEMBERS) members and
+ * the prefix stays at least max(min_prefix, block_size) tokens and keeps the
+ * page reads saved (prefix * members) from falling.  Groups of one are
+ * dropped.
+ *
+ *   block_tables     host int32 [num_seqs][max_blocks_per_seq].
+ *   context_lens     host int32 [num_seqs], each in [0, max_blocks_per_seq *
+ *                    block_size] (else PA_ERR_INVALID_ARG).
+ *   groups           host int32 [num_seqs][3] out: per group (first
+ *                    sequence, members, prefix tokens); rows past
+ *                    *num_groups are untouched.
+ *   seq_prefix_lens  host int32 [num_seqs] out: the prefix of the sequence's
+ *                    group, 0 for a sequence in no group.
+ *   num_groups, max_prefix_len  out.
+ */
+int pa_prefix_plan(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                   const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
+                   int32_t max_members, int32_t min_prefix, int32_t* groups,
+                   int32_t* seq_prefix_lens, int32_t* num_groups, int32_t* max_prefix_len);
+
+/*
+ * pa_decode_shared_prefix_workspace_bytes -- device workspace of
+ * pa_decode_shared_prefix: fp32 partials for ceil(max_prefix_len / partition)
+ * prefix partitions plus ceil(max_context_len / partition) others per
+ * (sequence, head); 0 when that is at most one.  partition 0 means one
+ * partition covering max_context_len, as in pa_decode.
+ */
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                               int32_t head_dim, int32_t max_context_len,
+                                               int32_t max_prefix_len, int32_t partition);
+
+/*
+ * pa_decode_shared_prefix -- pa_decode for a batch with prefix groups.
+ *
+ * Arguments as for pa_decode, plus (device memory, as pa_prefix_plan returns
+ * them, copied to the device):
+ *   prefix_groups    device int32 [num_groups][3]: (first sequence, members,
+ *                    prefix tokens).  Preconditions: members in
+ *                    1..PA_PREFIX_MAX_MEMBERS, groups disjoint, the prefix a
+ *                    multiple of block_size, at most every member's context,
+ *                    and every member's first prefix / block_size table
+ *                    entries equal to the first member's.
+ *   seq_prefix_lens  device int32 [num_seqs]: each sequence's group prefix,
+ *                    0 outside any group.
+ *   max_prefix_len   host: the largest prefix, a multiple of block_size and
+ *                    at most max_context_len.
+ * With num_groups == 0 or max_prefix_len == 0 the call is pa_decode (the two
+ * arrays may then be NULL).  A group's prefix pages are read from its first
+ * member's table in partitions of `partition` tokens, once for the queries
+ * of all members; each member's remaining tokens [prefix, L) are attended per
+ * sequence; the partials of both are merged per (sequence, head) in a fixed
+ * order (prefix partitions first), so the result is deterministic.  bf16,
+ * head_dim 128, num_heads / num_kv_heads in {1, 2, 4, 8}; anything else
+ * returns PA_ERR_UNSUPPORTED.  Violated preconditions give wrong results but
+ * no access outside the buffers pa_decode may touch.
+ */
+int pa_decode_shared_prefix(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int32_t num_blocks, float scale, int32_t partition,
+                            int32_t max_context_len, const int32_t* prefix_groups,
+                            int32_t num_groups, const int32_t* seq_prefix_lens,
+                            int32_t max_prefix_len, void* workspace, size_t workspace_bytes,
+                            int32_t dtype, void* stream);
+
+/*
  * pa_prefill_chunk -- causal attention of a chunk of query tokens per
  * sequence against that sequence's paged context (chunked prefill: the
  * prompt is processed in chunks whose KV accumulates in the cache, deep-dive

@@ -24,7 +24,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["allocator.cpp", "cache_ops.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["allocator.cpp", "prefix_plan.cpp", "cache_ops.hip", "decode.hip", "prefill.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",

@@ -99,12 +99,27 @@ struct Partials {
   float* ml;
 };
 
+// A sequence's tokens can be split between two passes at a page boundary:
+// [0, begin) -- a shared prefix, attended once for every sequence that shares
+// its blocks -- and [begin, L).  Each range is cut into partitions of
+// `partition` tokens.  The prefix's partials occupy partial slots
+// [0, prefix parts) of each (sequence, head) row and the rest's partials
+// slots [part_base, part_base + rest parts); a sequence whose two ranges make
+// only one partition in all has its output written directly.
+__device__ __forceinline__ int split_begin(int prefix, int L) {
+  return max(0, min(prefix, L)) & ~(kBS - 1);
+}
+__device__ __forceinline__ int split_parts(int begin, int L, int partition) {
+  return (begin + partition - 1) / partition + (L - begin + partition - 1) / partition;
+}
+
 template <typename T, int D, int G, bool PVB>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(
     T* __restrict__ out, Partials ws, const T* __restrict__ q, const T* __restrict__ kc,
     const T* __restrict__ vc, const int32_t* __restrict__ block_tables, int32_t max_blocks,
     const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t num_heads,
-    int32_t num_kv_heads, int32_t num_parts, int32_t partition, float scale_log2) {
+    int32_t num_kv_heads, int32_t num_parts, int32_t partition, float scale_log2,
+    const int32_t* __restrict__ starts, int32_t part_base) {
   using Gm = Geo<T, D>;
   constexpr int X = Gm::X, NKC = Gm::NKC, LPR = Gm::LPR, DPI = Gm::DPI, NVI = Gm::NVI;
   typedef typename std::conditional<PVB, uint16_t, float>::type p_t;
@@ -129,7 +144,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const int lane = threadIdx.x;
   const int h0 = g * G;
   const int L = context_lens[s];
-  const int part_start = part * partition;
   const int64_t out_row = (static_cast<int64_t>(s) * num_heads + h0) * D;
 
   if (L <= 0) {
@@ -137,9 +151,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
       for (int i = lane; i < G * D; i += 64) store_out<T>(out + out_row + i, 0.f);
     return;
   }
+  // Tokens [begin, L) of the sequence; [0, begin) is another pass's share.
+  const int begin = starts ? split_begin(starts[s], L) : 0;
+  const int part_start = begin + part * partition;
   if (part_start >= L) return;
   const int part_end = min(part_start + partition, L);
-  const int nparts_s = (L + partition - 1) / partition;
+  const int nparts_s = split_parts(begin, L, partition);
 
   // The G query rows (contiguous) are read-only and wave-uniform: reading them
   // through the constant address space turns them into scalar loads whose
@@ -400,7 +417,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
         if (nparts_s == 1) {
           store_out<T>(out + out_row + h * D + d, a * inv);
         } else {
-          const int64_t row = (static_cast<int64_t>(s) * num_heads + h0 + h) * num_parts + part;
+          const int64_t row =
+              (static_cast<int64_t>(s) * num_heads + h0 + h) * num_parts + part_base + part;
           ws.o[row * D + d] = a * inv;
         }
       }
@@ -409,7 +427,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   if (nparts_s > 1 && lane == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const int64_t row = (static_cast<int64_t>(s) * num_heads + h0 + h) * num_parts + part;
+      const int64_t row =
+          (static_cast<int64_t>(s) * num_heads + h0 + h) * num_parts + part_base + part;
       ws.ml[2 * row] = m[h];
       ws.ml[2 * row + 1] = lt[h];
     }
@@ -443,57 +462,35 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 // chunks); pages wholly past it re-read the step's first page (served from
 // L2) so every wave issues the same number of copies per step.  Block ids of
 // the first 64 pages of the partition are read once, into one register.
-template <int GW, int R, int W>
-__device__ __forceinline__ void group_item(
-    uint32_t li, pa::ring::StepBuf (&buf)[R], uint4 (&p_lds)[W][GW][4],
-    uint16_t* __restrict__ out, Partials ws, const uint16_t* __restrict__ q,
-    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
-    const int32_t* __restrict__ block_tables, int32_t max_blocks,
-    const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t num_heads,
-    int32_t num_kv_heads, int32_t num_parts, int32_t partition, float scale_log2) {
+// Attention of W * GW query rows over tokens [part_start, part_end) of one
+// block-table row, for kv head g: the pages stream through the LDS ring and
+// wave w serves local queries w*GW .. w*GW+GW-1.  qrow_of(i) gives local query
+// i's row; dest_of(i, out_off, part_row) where its result goes: the output
+// row at element offset out_off (>= 0), or partial row part_row (>= 0) of the
+// workspace, or nowhere (both -1).
+template <int GW, int R, int W, typename QRow, typename Dest>
+__device__ __forceinline__ void group_range(
+    pa::ring::StepBuf (&buf)[R], uint4 (&p_lds)[W][GW][4], uint16_t* __restrict__ out,
+    Partials ws, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const int32_t* __restrict__ bt_row, int32_t num_kv_heads, int g, int part_start, int part_end,
+    float scale_log2, QRow qrow_of, Dest dest_of) {
   using namespace pa::ring;
-  constexpr int G = W * GW;
   constexpr float kLazy = 8.f;  // log2 units
-
-  // same logical order as decode_kernel: kv head fastest, then sequence, then
-  // partition
-  const int g = static_cast<int>(li % static_cast<uint32_t>(num_kv_heads));
-  const uint32_t ps = li / static_cast<uint32_t>(num_kv_heads);
-  const int s = static_cast<int>(ps % static_cast<uint32_t>(num_seqs));
-  const int part = static_cast<int>(ps / static_cast<uint32_t>(num_seqs));
-  if (part >= num_parts) return;
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h0 = g * G;
-  const int L = context_lens[s];
-  const int part_start = part * partition;
-  const int64_t out_row = (static_cast<int64_t>(s) * num_heads + h0) * kD;
-  if (L <= 0) {
-    if (part == 0)
-      for (int i = tid; i < G * kD; i += W * 64) out[out_row + i] = 0;
-    return;
-  }
-  if (part_start >= L) return;
-  const int part_end = min(part_start + partition, L);
-  const int nparts_s = (L + partition - 1) / partition;
   const int nsteps = (part_end - part_start + kStep - 1) / kStep;
   const int npages = (part_end - part_start + kBS - 1) / kBS;
   const int lb_part = part_start / kBS;
-
   const int half = lane & 1;        // QK: which 64 dims
   const int tok = lane >> 1;        // QK: token of the step
   const int tg = lane >> 4;         // PV: token group (page tg / 2, tokens 8 * (tg % 2) ..)
   const int dl = lane & 15;         // PV: dims dl + 16 k
-  const int hw = h0 + wave * GW;    // first query head of this wave
-
-  const int32_t* bt_row = block_tables + static_cast<int64_t>(s) * max_blocks;
   int ids = bt_row[lb_part + min(lane, npages - 1)];  // block ids of pages 0..63
   uint4 qreg[GW][8];
 #pragma unroll
   for (int h = 0; h < GW; ++h) {
-    const uint16_t* qrow = q + (static_cast<int64_t>(s) * num_heads + hw + h) * kD + 64 * half;
+    const uint16_t* qrow = qrow_of(wave * GW + h) + 64 * half;
 #pragma unroll
     for (int c = 0; c < 8; ++c) qreg[h][c] = *reinterpret_cast<const uint4*>(qrow + 8 * c);
   }
@@ -600,12 +597,13 @@ __device__ __forceinline__ void group_item(
   for (int step = 0; step < nsteps - 1; ++step) do_step(step, std::false_type{});
   do_step(nsteps - 1, std::true_type{});
 
-  // ---- sum the four token groups; write the output or this partition's partial
+  // ---- sum the four token groups; write the output or a partial
 #pragma unroll
   for (int h = 0; h < GW; ++h) {
     const float lt = 0.5f * pa::wave_sum_u(lsum[h]);
     const float inv = 1.f / lt;
-    const int head = hw + h;
+    int64_t out_off, part_row;
+    dest_of(wave * GW + h, out_off, part_row);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       float a = acc[h][k];
@@ -613,21 +611,57 @@ __device__ __forceinline__ void group_item(
       a += __shfl_xor(a, 32, 64);
       const int d = dl + 16 * k;
       if (tg == 0) {
-        if (nparts_s == 1) {
-          out[(static_cast<int64_t>(s) * num_heads + head) * kD + d] =
-              static_cast<uint16_t>(pa::f32_to_bf16_bits(a * inv));
-        } else {
-          const int64_t row = (static_cast<int64_t>(s) * num_heads + head) * num_parts + part;
-          ws.o[row * kD + d] = a * inv;
-        }
+        if (out_off >= 0)
+          out[out_off + d] = static_cast<uint16_t>(pa::f32_to_bf16_bits(a * inv));
+        else if (part_row >= 0)
+          ws.o[part_row * kD + d] = a * inv;
       }
     }
-    if (nparts_s > 1 && lane == 0) {
-      const int64_t row = (static_cast<int64_t>(s) * num_heads + head) * num_parts + part;
-      ws.ml[2 * row] = m[h];
-      ws.ml[2 * row + 1] = lt;
+    if (part_row >= 0 && lane == 0) {
+      ws.ml[2 * part_row] = m[h];
+      ws.ml[2 * part_row + 1] = lt;
     }
   }
+}
+
+template <int GW, int R, int W>
+__device__ __forceinline__ void group_item(
+    uint32_t li, pa::ring::StepBuf (&buf)[R], uint4 (&p_lds)[W][GW][4],
+    uint16_t* __restrict__ out, Partials ws, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const int32_t* __restrict__ block_tables, int32_t max_blocks,
+    const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t num_parts, int32_t partition, float scale_log2,
+    const int32_t* __restrict__ starts, int32_t part_base) {
+  constexpr int G = W * GW;
+  // same logical order as decode_kernel: kv head fastest, then sequence, then
+  // partition
+  const int g = static_cast<int>(li % static_cast<uint32_t>(num_kv_heads));
+  const uint32_t ps = li / static_cast<uint32_t>(num_kv_heads);
+  const int s = static_cast<int>(ps % static_cast<uint32_t>(num_seqs));
+  const int part = static_cast<int>(ps / static_cast<uint32_t>(num_seqs));
+  if (part >= num_parts) return;
+
+  const int h0 = g * G;
+  const int L = context_lens[s];
+  const int64_t row0 = static_cast<int64_t>(s) * num_heads + h0;  // (seq, head) row of query 0
+  if (L <= 0) {
+    if (part == 0)
+      for (int i = threadIdx.x; i < G * pa::ring::kD; i += W * 64) out[row0 * pa::ring::kD + i] = 0;
+    return;
+  }
+  const int begin = starts ? split_begin(starts[s], L) : 0;
+  const int part_start = begin + part * partition;
+  if (part_start >= L) return;
+  const bool whole = split_parts(begin, L, partition) == 1;
+  group_range<GW, R, W>(
+      buf, p_lds, out, ws, kc, vc, block_tables + static_cast<int64_t>(s) * max_blocks,
+      num_kv_heads, g, part_start, min(part_start + partition, L), scale_log2,
+      [&](int i) { return q + (row0 + i) * pa::ring::kD; },
+      [&](int i, int64_t& out_off, int64_t& part_row) {
+        out_off = whole ? (row0 + i) * pa::ring::kD : -1;
+        part_row = whole ? -1 : (row0 + i) * num_parts + part_base + part;
+      });
 }
 
 // One workgroup per item (partition, sequence, kv head), in the one-wave
@@ -643,12 +677,80 @@ __global__ __launch_bounds__(W * 64) void decode_group_kernel(
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ block_tables, int32_t max_blocks,
     const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t num_heads,
-    int32_t num_kv_heads, int32_t num_parts, int32_t partition, float scale_log2) {
+    int32_t num_kv_heads, int32_t num_parts, int32_t partition, float scale_log2,
+    const int32_t* __restrict__ starts, int32_t part_base) {
   __shared__ pa::ring::StepBuf buf[kGroupRing];
   __shared__ uint4 p_lds[W][GW][4];  // per wave and head: 32 bf16 weights
-  group_item<GW, kGroupRing, W>(blockIdx.x, buf, p_lds, out, ws, q, kc, vc, block_tables, max_blocks,
-                 context_lens, num_seqs, num_heads, num_kv_heads, num_parts, partition,
-                 scale_log2);
+  group_item<GW, kGroupRing, W>(blockIdx.x, buf, p_lds, out, ws, q, kc, vc, block_tables,
+                                max_blocks, context_lens, num_seqs, num_heads, num_kv_heads,
+                                num_parts, partition, scale_log2, starts, part_base);
+}
+
+// Shared-prefix pass (bf16, head_dim 128).  Prefix group i is `count`
+// consecutive sequences starting at `first` whose block tables hold the same
+// physical blocks for the first `prefix` tokens (a multiple of the block
+// size) -- the samples of one prompt after a fork, or requests whose prompts
+// matched the same cached blocks.  Those tokens' K/V pages are read once, from
+// the first member's table, for the queries of every member: one workgroup
+// per (partition of the prefix, group, chunk of 8 queries, kv head), kv head
+// fastest, the queries of a kv head ordered (member, head within the kv
+// head's group).  Each query's partial result goes to partial slot `part` of
+// its (sequence, head) row, or straight to the output when the prefix is the
+// sequence's whole context and fits one partition.
+constexpr int kPrefixMembers = PA_PREFIX_MAX_MEMBERS;
+
+template <int GW, int W>
+__global__ __launch_bounds__(W * 64) void decode_prefix_kernel(
+    uint16_t* __restrict__ out, Partials ws, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const int32_t* __restrict__ block_tables, int32_t max_blocks,
+    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ groups,
+    int32_t num_groups, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t num_parts, int32_t prefix_parts, int32_t partition, float scale_log2) {
+  constexpr int Q = W * GW;  // queries per workgroup
+  __shared__ pa::ring::StepBuf buf[kGroupRing];
+  __shared__ uint4 p_lds[W][GW][4];
+  const int gq_heads = num_heads / num_kv_heads;
+  const int nchunks = (kPrefixMembers * gq_heads + Q - 1) / Q;
+  uint32_t li = blockIdx.x;
+  const int g = static_cast<int>(li % static_cast<uint32_t>(num_kv_heads));
+  li /= static_cast<uint32_t>(num_kv_heads);
+  const int chunk = static_cast<int>(li % static_cast<uint32_t>(nchunks));
+  li /= static_cast<uint32_t>(nchunks);
+  const int gi = static_cast<int>(li % static_cast<uint32_t>(num_groups));
+  const int part = static_cast<int>(li / static_cast<uint32_t>(num_groups));
+  if (part >= prefix_parts) return;
+
+  const int first = groups[3 * gi];
+  const int count = min(min(groups[3 * gi + 1], kPrefixMembers), num_seqs - first);
+  if (first < 0 || count <= 0) return;
+  const int P = split_begin(groups[3 * gi + 2], context_lens[first]);
+  const int part_start = part * partition;
+  const int nq = count * gq_heads;
+  const int q0 = chunk * Q;
+  if (part_start >= P || q0 >= nq) return;
+  const int n_pre = (P + partition - 1) / partition;
+  // (sequence, head) row of the chunk's local query i
+  auto row_of = [&](int i) -> int64_t {
+    const int gq = min(q0 + i, nq - 1);
+    const int s = first + gq / gq_heads;
+    return static_cast<int64_t>(s) * num_heads + g * gq_heads + gq % gq_heads;
+  };
+  group_range<GW, kGroupRing, W>(
+      buf, p_lds, out, ws, kc, vc, block_tables + static_cast<int64_t>(first) * max_blocks,
+      num_kv_heads, g, part_start, min(part_start + partition, P), scale_log2,
+      [&](int i) { return q + row_of(i) * pa::ring::kD; },
+      [&](int i, int64_t& out_off, int64_t& part_row) {
+        out_off = -1;
+        part_row = -1;
+        if (q0 + i >= nq) return;
+        const int64_t row = row_of(i);
+        const int s = first + (q0 + i) / gq_heads;
+        if (n_pre == 1 && context_lens[s] <= P)
+          out_off = row * pa::ring::kD;
+        else
+          part_row = row * num_parts + part;
+      });
 }
 
 // Second pass, one wave per (sequence, query head) with more than one
@@ -656,48 +758,60 @@ __global__ __launch_bounds__(W * 64) void decode_group_kernel(
 // M = max_p m_p.  Lane p computes partition p's weight (64 partitions at a
 // time); the partial outputs are then accumulated in partition order, each
 // lane owning D/64 consecutive dimensions, so the result is deterministic.
+// With a split sequence (starts != null) the partitions are the prefix's,
+// slots [0, n_pre), then the rest's, slots [part_base, part_base + n_rest).
 // (Merging inside the first pass would need an agent-scope release per
 // partition -- an L2 write-back on this chip, far costlier than this launch.)
 template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(
     T* __restrict__ out, Partials ws, const int32_t* __restrict__ context_lens, int32_t num_heads,
-    int32_t num_parts, int32_t partition) {
+    int32_t num_parts, int32_t partition, const int32_t* __restrict__ starts,
+    int32_t part_base) {
   constexpr int PER = D / 64;
   typedef float vec_t __attribute__((ext_vector_type(PER)));
   const int lane = threadIdx.x;
   const int64_t row = blockIdx.x;  // seq * num_heads + head
   const int s = static_cast<int>(row / num_heads);
   const int L = context_lens[s];
-  const int n = (L + partition - 1) / partition;
-  if (n <= 1) return;
+  if (L <= 0) return;
+  const int begin = starts ? split_begin(starts[s], L) : 0;
+  const int n_pre = (begin + partition - 1) / partition;
+  const int n_rest = (L - begin + partition - 1) / partition;
+  if (n_pre + n_rest <= 1) return;
   const int64_t row0 = row * num_parts;
   const float2* ml = reinterpret_cast<const float2*>(ws.ml) + row0;
   float M = -INFINITY;
-  for (int p = lane; p < n; p += 64) M = fmaxf(M, ml[p].x);
+  for (int p = lane; p < n_pre; p += 64) M = fmaxf(M, ml[p].x);
+  for (int p = lane; p < n_rest; p += 64) M = fmaxf(M, ml[part_base + p].x);
   M = pa::wave_max_u(M);
   const vec_t* po = reinterpret_cast<const vec_t*>(ws.o + row0 * D) + lane;
   vec_t acc = {};
   float wsum = 0.f;
-  for (int p0 = 0; p0 < n; p0 += 64) {
-    float w = 0.f;
-    if (p0 + lane < n) {
-      const float2 v = ml[p0 + lane];
-      w = v.y * pa::fast_exp2(v.x - M);
+  // partials [first, first + n) of the row, in order
+  auto run = [&](int first, int n) {
+    for (int p0 = 0; p0 < n; p0 += 64) {
+      float w = 0.f;
+      if (p0 + lane < n) {
+        const float2 v = ml[first + p0 + lane];
+        w = v.y * pa::fast_exp2(v.x - M);
+      }
+      wsum += w;
+      const int cnt = min(64, n - p0);
+      const vec_t* pj = po + (first + p0) * 64;
+      int j = 0;
+      for (; j + 4 <= cnt; j += 4) {  // four partitions' loads in flight
+        const vec_t o0 = pj[j * 64], o1 = pj[(j + 1) * 64], o2 = pj[(j + 2) * 64],
+                    o3 = pj[(j + 3) * 64];
+        acc += pa::readlane_f(w, j) * o0;
+        acc += pa::readlane_f(w, j + 1) * o1;
+        acc += pa::readlane_f(w, j + 2) * o2;
+        acc += pa::readlane_f(w, j + 3) * o3;
+      }
+      for (; j < cnt; ++j) acc += pa::readlane_f(w, j) * pj[j * 64];
     }
-    wsum += w;
-    const int cnt = min(64, n - p0);
-    const vec_t* pj = po + p0 * 64;
-    int j = 0;
-    for (; j + 4 <= cnt; j += 4) {  // four partitions' loads in flight
-      const vec_t o0 = pj[j * 64], o1 = pj[(j + 1) * 64], o2 = pj[(j + 2) * 64],
-                  o3 = pj[(j + 3) * 64];
-      acc += pa::readlane_f(w, j) * o0;
-      acc += pa::readlane_f(w, j + 1) * o1;
-      acc += pa::readlane_f(w, j + 2) * o2;
-      acc += pa::readlane_f(w, j + 3) * o3;
-    }
-    for (; j < cnt; ++j) acc += pa::readlane_f(w, j) * pj[j * 64];
-  }
+  };
+  run(0, n_pre);
+  run(part_base, n_rest);
   const float inv = 1.f / pa::wave_sum_u(wsum);
   T* dst = out + row * D + lane * PER;
 #pragma unroll
@@ -719,47 +833,64 @@ size_t ws_bytes(int64_t B, int64_t H, int64_t D, int64_t parts) {
          static_cast<size_t>(B * H * parts * 2) * sizeof(float);
 }
 
+Partials carve(void* ws, int64_t B, int64_t H, int64_t D, int64_t slots) {
+  Partials p{nullptr, nullptr};
+  if (slots > 1) {
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    p.o = reinterpret_cast<float*>(base);
+    base += align_up(static_cast<size_t>(B * H * slots * D) * sizeof(float));
+    p.ml = reinterpret_cast<float*>(base);
+  }
+  return p;
+}
+
+// Where a decode call's partitions go: `slots` partial slots per (sequence,
+// head) row; the first pass covers tokens [starts[s], L) (from 0 when starts
+// is null) in up to `parts` partitions written from slot part_base on.
+struct Split {
+  int32_t slots;
+  int32_t parts;
+  const int32_t* starts;
+  int32_t part_base;
+};
+
 template <typename T, int D, int G, bool PVB>
 int launch_decode(void* out, const void* q, const void* kc, const void* vc, const int32_t* bt,
                   int32_t max_blocks, const int32_t* lens, int32_t B, int32_t H, int32_t KVH,
-                  int32_t parts, int32_t partition, float scale_log2, void* ws, hipStream_t st) {
-  Partials p{nullptr, nullptr};
-  if (parts > 1) {
-    uint8_t* base = static_cast<uint8_t*>(ws);
-    p.o = reinterpret_cast<float*>(base);
-    base += align_up(static_cast<size_t>(B) * H * parts * D * sizeof(float));
-    p.ml = reinterpret_cast<float*>(base);
-  }
-  const int64_t grid = static_cast<int64_t>(parts) * KVH * B;
+                  Split sp, int32_t partition, float scale_log2, void* ws, hipStream_t st) {
+  const Partials p = carve(ws, B, H, D, sp.slots);
+  const int64_t grid = static_cast<int64_t>(sp.parts) * KVH * B;
   if constexpr (sizeof(T) == 2 && D == 128 && (G == 4 || G == 8)) {
     constexpr int W = G == 8 ? kGroupWaves8 : 4;
-    hipLaunchKernelGGL((decode_group_kernel<G / W, W>), dim3(static_cast<uint32_t>(grid)), dim3(W * 64),
-                       0, st, static_cast<uint16_t*>(out), p, static_cast<const uint16_t*>(q),
-                       static_cast<const uint16_t*>(kc), static_cast<const uint16_t*>(vc), bt,
-                       max_blocks, lens, B, H, KVH, parts, partition, scale_log2);
+    hipLaunchKernelGGL((decode_group_kernel<G / W, W>), dim3(static_cast<uint32_t>(grid)),
+                       dim3(W * 64), 0, st, static_cast<uint16_t*>(out), p,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
+                       static_cast<const uint16_t*>(vc), bt, max_blocks, lens, B, H, KVH, sp.slots,
+                       partition, scale_log2, sp.starts, sp.part_base);
   } else {
     hipLaunchKernelGGL((decode_kernel<T, D, G, PVB>), dim3(static_cast<uint32_t>(grid)), dim3(64),
                        0, st, static_cast<T*>(out), p, static_cast<const T*>(q),
                        static_cast<const T*>(kc), static_cast<const T*>(vc), bt, max_blocks, lens,
-                       B, H, KVH, parts, partition, scale_log2);
+                       B, H, KVH, sp.slots, partition, scale_log2, sp.starts, sp.part_base);
   }
-  if (parts > 1)
+  if (sp.slots > 1)
     hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(static_cast<uint32_t>(B) * H), dim3(64),
-                       0, st, static_cast<T*>(out), p, lens, H, parts, partition);
+                       0, st, static_cast<T*>(out), p, lens, H, sp.slots, partition, sp.starts,
+                       sp.part_base);
   return pa_launch_status();
 }
 
 template <typename T, int D>
 int dispatch_group(int G, void* out, const void* q, const void* kc, const void* vc,
                    const int32_t* bt, int32_t mb, const int32_t* lens, int32_t B, int32_t H,
-                   int32_t KVH, int32_t parts, int32_t partition, float sl2, void* ws,
+                   int32_t KVH, Split sp, int32_t partition, float sl2, void* ws,
                    hipStream_t st) {
   constexpr bool kBf = sizeof(T) == 2;
   switch (G) {
-    case 1: return launch_decode<T, D, 1, false>(out, q, kc, vc, bt, mb, lens, B, H, KVH, parts, partition, sl2, ws, st);
-    case 2: return launch_decode<T, D, 2, false>(out, q, kc, vc, bt, mb, lens, B, H, KVH, parts, partition, sl2, ws, st);
-    case 4: return launch_decode<T, D, 4, kBf>(out, q, kc, vc, bt, mb, lens, B, H, KVH, parts, partition, sl2, ws, st);
-    case 8: return launch_decode<T, D, 8, kBf>(out, q, kc, vc, bt, mb, lens, B, H, KVH, parts, partition, sl2, ws, st);
+    case 1: return launch_decode<T, D, 1, false>(out, q, kc, vc, bt, mb, lens, B, H, KVH, sp, partition, sl2, ws, st);
+    case 2: return launch_decode<T, D, 2, false>(out, q, kc, vc, bt, mb, lens, B, H, KVH, sp, partition, sl2, ws, st);
+    case 4: return launch_decode<T, D, 4, kBf>(out, q, kc, vc, bt, mb, lens, B, H, KVH, sp, partition, sl2, ws, st);
+    case 8: return launch_decode<T, D, 8, kBf>(out, q, kc, vc, bt, mb, lens, B, H, KVH, sp, partition, sl2, ws, st);
     default: return PA_ERR_UNSUPPORTED;
   }
 }
@@ -812,13 +943,102 @@ extern "C" int pa_decode(void* out, const void* q, const void* k_cache, const vo
   const int G = num_heads / num_kv_heads;
   const float sl2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int32_t P = static_cast<int32_t>(parts);
+  const Split sp{static_cast<int32_t>(parts), static_cast<int32_t>(parts), nullptr, 0};
   if (dtype == PA_BF16) {
     if (head_dim == 128)
-      return dispatch_group<uint16_t, 128>(G, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads, num_kv_heads, P, part, sl2, workspace, st);
-    return dispatch_group<uint16_t, 64>(G, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads, num_kv_heads, P, part, sl2, workspace, st);
+      return dispatch_group<uint16_t, 128>(G, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads, num_kv_heads, sp, part, sl2, workspace, st);
+    return dispatch_group<uint16_t, 64>(G, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads, num_kv_heads, sp, part, sl2, workspace, st);
   }
   if (head_dim == 128)
-    return dispatch_group<float, 128>(G, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads, num_kv_heads, P, part, sl2, workspace, st);
-  return dispatch_group<float, 64>(G, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads, num_kv_heads, P, part, sl2, workspace, st);
+    return dispatch_group<float, 128>(G, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads, num_kv_heads, sp, part, sl2, workspace, st);
+  return dispatch_group<float, 64>(G, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads, num_kv_heads, sp, part, sl2, workspace, st);
+}
+
+namespace {
+
+// Partial slots of a shared-prefix call: the prefix's partitions, then the
+// rest's.
+void shared_slots(int32_t max_context_len, int32_t max_prefix_len, int32_t part, int64_t& pre,
+                  int64_t& rest) {
+  pre = max_prefix_len > 0 ? parts_for(max_prefix_len, part) : 0;
+  rest = parts_for(max_context_len, part);
+}
+
+int32_t unsplit_partition(int32_t partition, int32_t max_context_len) {
+  if (partition != 0) return partition;
+  return static_cast<int32_t>(((std::max(max_context_len, 1) + kTile - 1) / kTile) * kTile);
+}
+
+}  // namespace
+
+extern "C" size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                                          int32_t head_dim,
+                                                          int32_t max_context_len,
+                                                          int32_t max_prefix_len,
+                                                          int32_t partition) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || partition < 0) return 0;
+  int64_t pre, rest;
+  shared_slots(max_context_len, max_prefix_len, unsplit_partition(partition, max_context_len), pre,
+               rest);
+  return ws_bytes(num_seqs, num_heads, head_dim, pre + rest);
+}
+
+extern "C" int pa_decode_shared_prefix(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t num_blocks, float scale, int32_t partition,
+    int32_t max_context_len, const int32_t* prefix_groups, int32_t num_groups,
+    const int32_t* seq_prefix_lens, int32_t max_prefix_len, void* workspace,
+    size_t workspace_bytes, int32_t dtype, void* stream) {
+  if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
+      num_blocks <= 0 || partition < 0 || max_context_len < 0 || num_groups < 0 ||
+      max_prefix_len < 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (dtype != PA_BF16 || block_size != kBS || head_dim != 128) return PA_ERR_UNSUPPORTED;
+  const int G = num_heads / num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
+  if (partition % kTile != 0 || max_prefix_len % kBS != 0 || max_prefix_len > max_context_len)
+    return PA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * kBS)
+    return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return PA_ERR_INVALID_ARG;
+  const bool split = num_groups > 0 && max_prefix_len > 0;
+  if (split && (!prefix_groups || !seq_prefix_lens)) return PA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
+       reinterpret_cast<uintptr_t>(v_cache)) & 15)
+    return PA_ERR_INVALID_ARG;
+  const int32_t part = unsplit_partition(partition, max_context_len);
+  int64_t pre, rest;
+  shared_slots(max_context_len, split ? max_prefix_len : 0, part, pre, rest);
+  const int64_t slots = pre + rest;
+  const int64_t nchunks = (static_cast<int64_t>(kPrefixMembers) * G + 7) / 8;
+  if (slots > 0x7fffffff || rest * num_kv_heads * num_seqs > 0x7fffffffLL ||
+      pre * num_groups * nchunks * num_kv_heads > 0x7fffffffLL)
+    return PA_ERR_INVALID_ARG;
+  const size_t need = ws_bytes(num_seqs, num_heads, head_dim, slots);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+  const float sl2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (split) {
+    const Partials p = carve(workspace, num_seqs, num_heads, 128, slots);
+    const int64_t grid = pre * num_groups * nchunks * num_kv_heads;
+    hipLaunchKernelGGL((decode_prefix_kernel<2, 4>), dim3(static_cast<uint32_t>(grid)), dim3(256),
+                       0, st, static_cast<uint16_t*>(out), p, static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(k_cache),
+                       static_cast<const uint16_t*>(v_cache), block_tables, max_blocks_per_seq,
+                       context_lens, prefix_groups, num_groups, num_seqs, num_heads, num_kv_heads,
+                       static_cast<int32_t>(slots), static_cast<int32_t>(pre), part, sl2);
+    const int rc = pa_launch_status();
+    if (rc != PA_OK) return rc;
+  }
+  const Split sp{static_cast<int32_t>(slots), static_cast<int32_t>(rest),
+                 split ? seq_prefix_lens : nullptr, static_cast<int32_t>(pre)};
+  return dispatch_group<uint16_t, 128>(G, out, q, k_cache, v_cache, block_tables,
+                                       max_blocks_per_seq, context_lens, num_seqs, num_heads,
+                                       num_kv_heads, sp, part, sl2, workspace, st);
 }

@@ -141,6 +141,95 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float
         _stream(q)))
 
 
+def pa_prefix_plan(block_tables, context_lens, max_members: int = 8, min_prefix: int = 256,
+                   block_size: int = BLOCK_SIZE):
+    """Prefix groups of a batch (host arrays or tensors; runs on the host).
+
+    Returns (groups int32 [num_groups, 3] = (first sequence, members, prefix
+    tokens), seq_prefix_lens int32 [num_seqs], max_prefix_len)."""
+    bt = np.ascontiguousarray(np.asarray(block_tables.cpu() if torch.is_tensor(block_tables)
+                                         else block_tables, dtype=np.int32))
+    lens = np.ascontiguousarray(np.asarray(context_lens.cpu() if torch.is_tensor(context_lens)
+                                           else context_lens, dtype=np.int32))
+    if bt.ndim != 2 or lens.shape != (bt.shape[0],):
+        raise ValueError("block_tables must be [B, max_blocks] and context_lens [B]")
+    B = bt.shape[0]
+    groups = np.zeros((max(B, 1), 3), dtype=np.int32)
+    pre = np.zeros(max(B, 1), dtype=np.int32)
+    ng = np.zeros(1, dtype=np.int32)
+    mp = np.zeros(1, dtype=np.int32)
+    check("pa_prefix_plan", lib().pa_prefix_plan(
+        bt.ctypes.data, bt.shape[1], lens.ctypes.data, B, int(block_size), int(max_members),
+        int(min_prefix), groups.ctypes.data, pre.ctypes.data, ng.ctypes.data, mp.ctypes.data))
+    return groups[: int(ng[0])].copy(), pre[:B].copy(), int(mp[0])
+
+
+def pa_decode_shared_prefix_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len,
+                                            max_prefix_len, partition) -> int:
+    return int(lib().pa_decode_shared_prefix_workspace_bytes(
+        num_seqs, num_heads, head_dim, max_context_len, max_prefix_len, partition))
+
+
+def pa_decode_shared_prefix(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                            partition: int, max_context_len: int, prefix_groups,
+                            seq_prefix_lens, max_prefix_len: int, workspace=None,
+                            check_device_args=False):
+    """pa_decode with prefix groups (device int32 tensors [G, 3] and [B], as
+    pa_prefix_plan returns them)."""
+    nb, kvh, d, bs = _cache_dims(k_cache, v_cache)
+    B, H = q.shape[0], q.shape[1]
+    if q.shape != (B, H, d) or out.shape != q.shape or not (q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("q/out must be contiguous [B, H, head_dim]")
+    if q.dtype != k_cache.dtype or out.dtype != q.dtype:
+        raise TypeError("q/out dtype must match the cache")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B \
+            or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be contiguous int32 [B, max_blocks]")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (B,):
+        raise ValueError("context_lens must be int32 [B]")
+    ng = int(prefix_groups.shape[0])
+    if prefix_groups.dtype != torch.int32 or prefix_groups.dim() != 2 or prefix_groups.shape[1] != 3 \
+            or not prefix_groups.is_contiguous():
+        raise ValueError("prefix_groups must be contiguous int32 [num_groups, 3]")
+    if seq_prefix_lens.dtype != torch.int32 or seq_prefix_lens.shape != (B,):
+        raise ValueError("seq_prefix_lens must be int32 [B]")
+    if check_device_args:
+        _check_tables(block_tables, context_lens, nb, bs)
+        if int(context_lens.max()) > max_context_len:
+            raise ValueError("max_context_len below a context length")
+        _check_groups(block_tables.cpu().numpy(), context_lens.cpu().numpy(),
+                      prefix_groups.cpu().numpy(), seq_prefix_lens.cpu().numpy(), max_prefix_len, bs)
+    need = pa_decode_shared_prefix_workspace_bytes(B, H, d, max_context_len, max_prefix_len,
+                                                   partition)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    check("pa_decode_shared_prefix", lib().pa_decode_shared_prefix(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(), B, H, kvh, d, bs,
+        nb, float(scale), int(partition), int(max_context_len),
+        prefix_groups.data_ptr() if ng else None, ng,
+        seq_prefix_lens.data_ptr(), int(max_prefix_len), wptr, wbytes, _dtype(q), _stream(q)))
+
+
+def _check_groups(bt, lens, groups, pre, max_prefix_len, bs):
+    covered = np.zeros(bt.shape[0], dtype=bool)
+    expect = np.zeros(bt.shape[0], dtype=np.int64)
+    for first, n, P in groups:
+        if not (1 <= n <= 8) or first < 0 or first + n > bt.shape[0] or P % bs or P > max_prefix_len:
+            raise ValueError(f"bad prefix group {(first, n, P)}")
+        if covered[first:first + n].any():
+            raise ValueError("prefix groups overlap")
+        covered[first:first + n] = True
+        expect[first:first + n] = P
+        for s in range(first, first + n):
+            if lens[s] < P or (bt[s, : P // bs] != bt[first, : P // bs]).any():
+                raise ValueError(f"sequence {s} does not share group {first}'s prefix")
+    if (pre != expect).any():
+        raise ValueError("seq_prefix_lens disagrees with prefix_groups")
+
+
 def pa_prefill_chunk(out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens,
                      max_query_len: int, scale: float, check_device_args=False):
     nb, kvh, d, bs = _cache_dims(k_cache, v_cache)

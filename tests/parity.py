@@ -7,7 +7,8 @@ import numpy as np
 import torch
 
 from oracle import run
-from paged_kv_cache_219_amd.kernels import pa_decode, pa_prefill_chunk
+from paged_kv_cache_219_amd.kernels import (pa_decode, pa_decode_shared_prefix, pa_prefill_chunk,
+                                            pa_prefix_plan)
 from paged_kv_cache_219_amd.workload import DeviceWorkload, to_host_bits
 
 # Tolerances for the attention output: fp32 inputs max |err| <= 1e-5; bf16
@@ -48,9 +49,11 @@ def assert_pool_equal(w: DeviceWorkload, st) -> None:
     assert np.array_equal(raw_bits(gv), raw_bits(st.v_cache)), "v_cache differs from the oracle"
 
 
-def gpu_step(script, partition=None, scale=None, step=0, workload=None):
+def gpu_step(script, partition=None, scale=None, step=0, workload=None, shared_prefix=None):
     """Run the script's setup and step on the GPU; return (workload, out,
-    host tables, host lens)."""
+    host tables, host lens).  ``shared_prefix`` = (max_members, min_prefix)
+    runs decode through pa_decode_shared_prefix with the groups
+    pa_prefix_plan finds (kept in ``w.prefix_plan``)."""
     w = workload or DeviceWorkload(script)
     w.run_step()
     bt, lens, bt_h, lens_h = w.batch_tables()
@@ -60,8 +63,17 @@ def gpu_step(script, partition=None, scale=None, step=0, workload=None):
     sc = s.scale if scale is None else scale
     if s.kind == "decode":
         part = s.partition if partition is None else partition
-        pa_decode(out, q, w.k_cache, w.v_cache, bt, lens, sc, part, int(max(lens_h.max(), 0)),
-                  check_device_args=True)
+        if shared_prefix is None:
+            pa_decode(out, q, w.k_cache, w.v_cache, bt, lens, sc, part, int(max(lens_h.max(), 0)),
+                      check_device_args=True)
+        else:
+            groups, pre, mp = pa_prefix_plan(bt_h, lens_h, *shared_prefix)
+            w.prefix_plan = (groups, pre, mp)
+            pa_decode_shared_prefix(out, q, w.k_cache, w.v_cache, bt, lens, sc, part,
+                                    int(max(lens_h.max(), 0)),
+                                    torch.from_numpy(groups).to(q.device),
+                                    torch.from_numpy(pre).to(q.device), mp,
+                                    check_device_args=True)
     else:
         pa_prefill_chunk(out, q, w.k_cache, w.v_cache, bt, w.query_start_loc(), lens,
                          max(script.query_lens), sc, check_device_args=True)

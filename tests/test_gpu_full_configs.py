@@ -30,12 +30,16 @@ def _sample_seqs(lens, k=4, seed=0):
 
 
 @pytest.mark.parametrize("name", ["decode_bf16", "gqa_decode_bf16", "shared_prefix_bf16",
-                                  "chunked_prefill_bf16"])
+                                  "shared_prefix_bf16:grouped", "chunked_prefill_bf16"])
 def test_full_size_sampled(name):
     say(f"full-size {name}: building on GPU")
+    name, _, mode = name.partition(":")
     sc = config_script(name)
     s = sc.spec
-    w, out, bt_h, lens_h = gpu_step(sc)
+    # grouped: through pa_decode_shared_prefix with the planner's default groups
+    w, out, bt_h, lens_h = gpu_step(sc, shared_prefix=(8, 256) if mode else None)
+    if mode:
+        assert len(w.prefix_plan[0]) == len(sc.batch) // 8
     assert torch.isfinite(out.float()).all()
     seqs = _sample_seqs(lens_h)
     g = np.random.default_rng(1)

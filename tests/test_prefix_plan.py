@@ -1,0 +1,160 @@
+"""Host-side checks of the prefix-group planner (pa_prefix_plan) and of the
+shared-prefix decode's argument checks (no GPU needed).
+
+The planner's groups are pinned to structure known by construction: block
+tables built with shared prefix blocks, and the block tables the oracle's
+allocator model produces for the parallel-sampling scripts (each prompt's
+samples share the prompt's whole blocks; with a partial last prompt block,
+the samples copy it on their first write and share one block less).
+"""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+from oracle import run
+from paged_kv_cache_219_amd import lib
+from paged_kv_cache_219_amd._lib import PA_BF16, PA_F32
+from paged_kv_cache_219_amd.kernels import pa_prefix_plan
+from synth import config_script
+
+BS = 16
+
+
+def _tables(spec_groups, g, nb=4096):
+    """spec_groups: list of (prefix tokens, [context lengths of the members])."""
+    ids = iter(g.permutation(nb).tolist())
+    rows, lens = [], []
+    for prefix, Ls in spec_groups:
+        shared = [next(ids) for _ in range(prefix // BS)]
+        for L in Ls:
+            rows.append(shared + [next(ids) for _ in range(-(-L // BS) - len(shared))])
+            lens.append(L)
+    mb = max(1, max(len(r) for r in rows))
+    bt = np.full((len(rows), mb), -1, np.int32)
+    for i, r in enumerate(rows):
+        bt[i, : len(r)] = r
+    return bt, np.array(lens, np.int32)
+
+
+def _valid(bt, lens, groups, pre, max_members, min_prefix):
+    covered = np.zeros(len(lens), bool)
+    expect = np.zeros(len(lens), np.int64)
+    last = -1
+    for first, n, P in groups.tolist():
+        assert first > last and 2 <= n <= max_members
+        assert P % BS == 0 and P >= max(min_prefix, BS)
+        assert not covered[first:first + n].any()
+        covered[first:first + n] = True
+        expect[first:first + n] = P
+        for s in range(first, first + n):
+            assert lens[s] >= P
+            assert (bt[s, : P // BS] == bt[first, : P // BS]).all()
+        last = first + n - 1
+    assert (pre == expect).all()
+
+
+def test_planner_finds_constructed_groups():
+    g = np.random.default_rng(0)
+    bt, lens = _tables([(512, [513, 600, 512]), (0, [40]), (32, [33, 40]), (0, [0]),
+                        (48, [48, 48, 60])], g)
+    groups, pre, mp = pa_prefix_plan(bt, lens, 8, 16)
+    assert groups.tolist() == [[0, 3, 512], [4, 2, 32], [7, 3, 48]]
+    assert pre.tolist() == [512] * 3 + [0] + [32] * 2 + [0] + [48] * 3
+    assert mp == 512
+
+
+def test_planner_thresholds_and_member_cap():
+    g = np.random.default_rng(1)
+    bt, lens = _tables([(256, [300] * 8)], g)
+    assert pa_prefix_plan(bt, lens, 8, 512)[0].shape == (0, 3)    # prefix below min_prefix
+    groups = pa_prefix_plan(bt, lens, 3, 16)[0].tolist()
+    assert groups == [[0, 3, 256], [3, 3, 256], [6, 2, 256]]
+    assert pa_prefix_plan(bt, lens, 1, 16)[0].shape == (0, 3)      # groups of one are dropped
+
+
+def test_planner_keeps_reads_saved_from_falling():
+    # member 1 shares 64 blocks with the leader, member 2 only 16: joining
+    # would cut the prefix from 1024 to 256 tokens, and the reads saved from
+    # 1 x 1024 to 2 x 256, so member 2 stays out.
+    g = np.random.default_rng(2)
+    bt, lens = _tables([(1024, [1030, 1100])], g, nb=8192)
+    row = np.concatenate([bt[0, :16], g.permutation(np.arange(5000, 8000))[:60]]).astype(np.int32)
+    bt = np.vstack([np.pad(bt, ((0, 0), (0, max(0, len(row) - bt.shape[1]))), constant_values=-1)])
+    row = np.pad(row, (0, bt.shape[1] - len(row)), constant_values=-1)
+    bt = np.vstack([bt, row[None]])
+    lens = np.append(lens, 960).astype(np.int32)
+    groups, pre, _ = pa_prefix_plan(bt, lens, 8, 16)
+    assert groups.tolist() == [[0, 2, 1024]]
+    assert pre.tolist() == [1024, 1024, 0]
+
+
+@pytest.mark.parametrize("name,prefix", [("shared_prefix_bf16", 1024),
+                                         ("shared_prefix_cow_bf16", 1008)])
+def test_planner_on_parallel_sampling_tables(name, prefix):
+    sc = config_script(name, scale_down=16)
+    st = run.build(sc, only_seqs=[])
+    tables, lens = run.batch_tables(st, sc)
+    groups, pre, mp = pa_prefix_plan(tables, lens, 8, 256)
+    prompts = len(sc.batch) // 8
+    assert groups.tolist() == [[8 * p, 8, prefix] for p in range(prompts)]
+    assert mp == prefix
+    _valid(tables, lens, groups, pre, 8, 256)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_planner_groups_are_valid_on_random_sharing(seed):
+    g = np.random.default_rng(100 + seed)
+    spec = []
+    for _ in range(int(g.integers(1, 12))):
+        prefix = BS * int(g.integers(0, 40))
+        n = int(g.integers(1, 11))
+        spec.append((prefix, [prefix + int(g.integers(0, 50)) for _ in range(n)]))
+    bt, lens = _tables(spec, g)
+    for mm, mp in ((8, 16), (4, 64), (2, 16)):
+        groups, pre, maxp = pa_prefix_plan(bt, lens, mm, mp)
+        _valid(bt, lens, groups, pre, mm, mp)
+        assert maxp == (int(groups[:, 2].max()) if len(groups) else 0)
+
+
+def test_planner_rejects_bad_arguments():
+    L = lib()
+    bt = np.zeros((2, 4), np.int32)
+    lens = np.array([16, 65], np.int32)  # 65 > 4 blocks x 16
+    out = np.zeros(8, np.int32)
+    n = np.zeros(2, np.int32)
+    p = lambda a: a.ctypes.data
+    assert L.pa_prefix_plan(p(bt), 4, p(lens), 2, 16, 8, 16, p(out), p(out), p(n), p(n[1:])) == -1
+    lens[1] = 64
+    assert L.pa_prefix_plan(p(bt), 4, p(lens), 2, 16, 9, 16, p(out), p(out), p(n), p(n[1:])) == -1
+    assert L.pa_prefix_plan(p(bt), 4, p(lens), 2, 16, 0, 16, p(out), p(out), p(n), p(n[1:])) == -1
+    assert L.pa_prefix_plan(p(bt), 4, p(lens), 2, 16, 8, 16, p(out), p(out), p(n), p(n[1:])) == 0
+    assert n.tolist() == [1, 16]  # identical tables: one group over the first block
+
+
+def test_shared_prefix_decode_rejects_before_launch():
+    L = lib()
+    fake = ctypes.c_void_p(16)  # never dereferenced: every call fails validation first
+
+    def dec(**kw):
+        a = dict(mb=8, B=2, H=8, KVH=8, D=128, BS=16, NB=64, part=64, maxL=100, ng=1, maxP=64,
+                 dt=PA_BF16)
+        a.update(kw)
+        return L.pa_decode_shared_prefix(fake, fake, fake, fake, fake, a["mb"], fake, a["B"], a["H"],
+                                         a["KVH"], a["D"], a["BS"], a["NB"], 0.1, a["part"],
+                                         a["maxL"], fake, a["ng"], fake, a["maxP"], None, 0,
+                                         a["dt"], None)
+    assert dec() == -6                      # needs a workspace
+    assert dec(dt=PA_F32) == -5             # bf16 only
+    assert dec(D=64) == -5                  # head_dim 128 only
+    assert dec(H=24) == -5                  # query groups of 3 heads
+    assert dec(maxP=40) == -1               # prefix not whole blocks
+    assert dec(maxP=112) == -1              # prefix longer than any context
+    assert dec(part=100) == -1
+    assert dec(ng=-1) == -1
+    ws = L.pa_decode_shared_prefix_workspace_bytes
+    # prefix partitions + context partitions, fp32 (D + 2) per slot, aligned
+    assert ws(2, 8, 128, 100, 64, 64) == 2 * 8 * 3 * 128 * 4 + 2 * 8 * 3 * 2 * 4
+    assert ws(2, 8, 128, 100, 0, 0) == 0    # one partition, no prefix
+    assert ws(2, 8, 128, 100, 64, 0) > 0    # prefix + rest: two partials to merge
