@@ -199,10 +199,10 @@ int pa_prefix_plan(const int32_t* block_tables, int32_t max_blocks_per_seq,
 
 /*
  * pa_decode_shared_prefix_workspace_bytes -- device workspace of
- * pa_decode_shared_prefix: fp32 partials for ceil(max_prefix_len / partition)
- * prefix partitions plus ceil(max_context_len / partition) others per
- * (sequence, head); 0 when that is at most one.  partition 0 means one
- * partition covering max_context_len, as in pa_decode.
+ * pa_decode_shared_prefix: fp32 partials for ceil(max_prefix_len /
+ * (2 * partition)) prefix partitions plus ceil(max_context_len / partition)
+ * others per (sequence, head); 0 when that is at most one.  partition 0 means
+ * one partition covering max_context_len, as in pa_decode.
  */
 size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads,
                                                int32_t head_dim, int32_t max_context_len,
@@ -225,7 +225,7 @@ size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_hea
  *                    at most max_context_len.
  * With num_groups == 0 or max_prefix_len == 0 the call is pa_decode (the two
  * arrays may then be NULL).  A group's prefix pages are read from its first
- * member's table in partitions of `partition` tokens, once for the queries
+ * member's table in partitions of 2 * partition tokens, once for the queries
  * of all members; each member's remaining tokens [prefix, L) are attended per
  * sequence; the partials of both are merged per (sequence, head) in a fixed
  * order (prefix partitions first), so the result is deterministic.  bf16,
