@@ -26,6 +26,7 @@ import os
 import re
 import sys
 import time
+from types import SimpleNamespace
 
 import numpy as np
 
@@ -268,6 +269,80 @@ def bench_prefill(name: str, steps: int, warmup: int):
     return res
 
 
+def bench_prefix_cache(steps: int, warmup: int):
+    """Automatic prefix caching on multi-turn chat requests (16 dialogues x 4
+    turns, a 1024-token common system prompt, 64-token user turns, 192-token
+    answers): the allocator's hit rate and host time per request over all
+    turns, and the last turn's 16 prompts prefilled in one pa_prefill_chunk
+    launch twice -- only the uncached tokens as queries (the cache holding the
+    rest), and every prompt token as a query."""
+    import torch
+
+    from paged_kv_cache_219_amd import BlockAllocator
+    from paged_kv_cache_219_amd.kernels import new_kv_cache, pa_prefill_chunk
+    from synth import multi_turn_requests
+
+    bs, H, D = 16, 32, 128
+    reqs = multi_turn_requests(6, dialogues=16, turns=4, system_len=1024, user_len=64,
+                               answer_len=192, vocab=32000)
+    last = [r for r in reqs if r[1] == 3]
+    need = sum(-(-(len(p) + len(a)) // bs) for _, _, p, a in reqs)
+    nb = need  # room for every history: nothing is evicted
+    alloc = BlockAllocator(nb, bs, np.random.default_rng(6).permutation(nb).astype(np.int32))
+    alloc.enable_prefix_cache()
+    t_host = 0.0
+    live = []
+    for i, (_, turn, prompt, answer) in enumerate(reqs):
+        t = time.perf_counter()
+        rc, hit = alloc.new_cached(i, prompt)
+        rc2, _, _ = alloc.append_tokens(i, prompt[hit:])
+        t_host += time.perf_counter() - t
+        assert rc == 0 and rc2 == 0
+        if turn == 3:
+            live.append((i, hit, len(prompt)))
+            continue
+        alloc.append_tokens(i, answer)
+        alloc.free(i)
+    stats = alloc.prefix_cache_stats()
+    mb = max(-(-n // bs) for _, _, n in live)
+    tables, lens = alloc.export_tables([i for i, _, _ in live], mb)
+    dev = torch.device("cuda")
+    kc, vc = new_kv_cache(nb, H, D, torch.bfloat16, dev)
+    kc.normal_()
+    vc.normal_()
+    bt = torch.from_numpy(tables).to(dev)
+    ln = torch.from_numpy(lens).to(dev)
+    stream = torch.cuda.current_stream(dev)
+    scale = float(np.float32(1 / np.sqrt(D)))
+    res = {"workload": "prefix_cache_multi_turn_bf16", "requests": len(reqs),
+           "hit_rate": stats["hit_tokens"] / stats["query_tokens"],
+           "host_us_per_request": 1e6 * t_host / len(reqs), "cache_stats": stats}
+    for mode in ("cached", "recompute"):
+        nq = [n - h if mode == "cached" else n for _, h, n in live]
+        qsl = torch.tensor(np.concatenate([[0], np.cumsum(nq)]).astype(np.int32), device=dev)
+        q = torch.randn((int(sum(nq)), H, D), device=dev).to(torch.bfloat16)
+        out = torch.empty_like(q)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for it in range(warmup + steps):
+            if it >= warmup:
+                ev[it - warmup][0].record(stream)
+            pa_prefill_chunk(out, q, kc, vc, bt, qsl, ln, max(nq), scale)
+            if it >= warmup:
+                ev[it - warmup][1].record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        flops = prefill_flops([n - k for k, (_, _, n) in zip(nq, live)], nq,
+                              SimpleNamespace(head_dim=D, num_heads=H))
+        res[f"{mode}_query_tokens"] = int(sum(nq))
+        res[f"{mode}_prefill_ms"] = ms
+        res[f"{mode}_TFLOPs"] = flops / (ms * 1e-3) / 1e12
+    res["prefill_speedup"] = res["recompute_prefill_ms"] / res["cached_prefill_ms"]
+    del kc, vc
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(budget_s: float = 10.0, max_passes: int = 8):
     """The fp64 numpy oracle decoding the headline workload's batch, four
     sequences at a time, single-threaded (BLAS pinned to one thread).  The
@@ -439,6 +514,8 @@ def run_workload(spec: str, steps: int, warmup: int):
     name, _, mode = spec.partition(":")
     if mode not in ("", "grouped"):
         raise SystemExit(f"unknown workload mode {mode!r}")
+    if name == "prefix_cache_multi_turn_bf16":
+        return bench_prefix_cache(steps, warmup)
     if "prefill" in name:
         return bench_prefill(name, steps, warmup)
     return bench_decode(name, steps, warmup, grouped=mode == "grouped")
@@ -451,7 +528,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--configs",
                     default="gqa_decode_bf16,shared_prefix_bf16,shared_prefix_bf16:grouped,"
-                            "chunked_prefill_bf16",
+                            "chunked_prefill_bf16,prefix_cache_multi_turn_bf16",
                     help="extra workloads reported under 'workloads' ('' for none); a decode "
                          "workload suffixed ':grouped' runs through pa_decode_shared_prefix")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -484,7 +561,12 @@ def main():
     extras = []
     for name in [c for c in a.configs.split(",") if c]:
         r = run_workload(name, a.steps, a.warmup)
-        if "prefill" in name:
+        if name == "prefix_cache_multi_turn_bf16":
+            print(f"[bench] {name}: hit rate {r['hit_rate']:.3f}, "
+                  f"{r['host_us_per_request']:.1f} us/request on the host; last-turn prefill "
+                  f"{r['cached_prefill_ms']:.3f} ms cached vs {r['recompute_prefill_ms']:.3f} ms "
+                  f"recomputed", file=sys.stderr, flush=True)
+        elif "prefill" in name:
             print(f"[bench] {name}: {r['prefill_ms']:.3f} ms = {r['prefill_TFLOPs']:.1f} TFLOP/s",
                   file=sys.stderr, flush=True)
         else:

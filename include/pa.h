@@ -337,12 +337,74 @@ int pa_export_tables(const pa_allocator* a, const int64_t* seqs, int32_t num_seq
                      int32_t* context_lens_out);
 
 /*
- * pa_alloc_stats -- out[0] free blocks, out[1] blocks in use, out[2] blocks
+ * pa_alloc_stats -- out[0] free blocks (on the free list), out[1] the rest
+ * (held by a sequence or kept by the prefix cache), out[2] blocks
  * with more than one reference, out[3] live sequences, out[4] wasted slots
  * (internal fragmentation: sum over sequences of blocks_held * block_size -
  * length; below block_size per sequence).
  */
 int pa_alloc_stats(const pa_allocator* a, int64_t out[5]);
+
+/* ------------------------------------------------ automatic prefix caching */
+
+/*
+ * Automatic prefix caching (deep-dive page, section "Cơ chế APC", items 1-2:
+ * a trie of cached KV blocks; a new request whose prefix matches links the
+ * matched physical blocks into its table instead of recomputing them; and
+ * its advice to evict blocks not recently used under memory pressure).
+ *
+ * Granularity is whole blocks: a trie node is one full block's token ids
+ * under its parent (the blocks before it).  Rules:
+ *  - A block enters the trie when it becomes full through
+ *    pa_seq_append_tokens (token ids known for the whole sequence so far) and
+ *    no node with the same tokens exists under the same parent; otherwise it
+ *    stays private.  Appends without token ids (pa_seq_append,
+ *    pa_batch_append) end caching for that sequence.
+ *  - pa_seq_new_cached matches the prompt's full blocks from the root,
+ *    leaving at least the last prompt token uncached (at most (n - 1) /
+ *    block_size blocks), links the matched blocks (one more reference each)
+ *    and starts the sequence at the matched length.
+ *  - A cached block that no sequence holds any more is kept; the free list is
+ *    used first, and only when it is empty is a kept block evicted: least
+ *    recently used first (use = matched, registered or released), the deeper
+ *    block first among equals, then the lower block id.  Evicting a block
+ *    drops its trie node and everything under it; their blocks become
+ *    ordinary blocks (to the free list if no sequence holds them).
+ *  - Out of blocks means free list plus kept blocks cannot cover a request.
+ * The hit rate is hit tokens / prompt tokens over pa_seq_new_cached calls.
+ */
+
+/* Turn prefix caching on; only while the allocator holds no sequence. */
+int pa_alloc_enable_prefix_cache(pa_allocator* a);
+
+/*
+ * pa_seq_new_cached -- new sequence `seq` for a prompt of n tokens (host
+ * int32 token ids).  *n_cached_out = tokens found in the cache (a multiple of
+ * block_size); the sequence starts with that length, and the caller appends
+ * the remaining n - *n_cached_out prompt tokens with pa_seq_append_tokens.
+ * PA_ERR_INVALID_ARG if caching is off.
+ */
+int pa_seq_new_cached(pa_allocator* a, int64_t seq, const int32_t* tokens, int32_t n,
+                      int32_t* n_cached_out);
+
+/* pa_seq_append with the appended tokens' ids (host int32 [n]). */
+int pa_seq_append_tokens(pa_allocator* a, int64_t seq, const int32_t* tokens, int32_t n,
+                         int64_t* slots_out, int32_t* cow_pair_out, int32_t* n_cow_out);
+
+/*
+ * pa_prefix_cache_stats -- out[0] hit tokens, out[1] prompt tokens looked up,
+ * out[2] blocks in the trie, out[3] of those, blocks no sequence holds,
+ * out[4] evictions.
+ */
+int pa_prefix_cache_stats(const pa_allocator* a, int64_t out[5]);
+
+/*
+ * pa_prefix_cache_blocks -- the blocks in the trie, by block id, with their
+ * depth (logical block index + 1), and optionally (evictable_out, same cap)
+ * the kept blocks in eviction order.  *n_out = number of blocks in the trie.
+ */
+int pa_prefix_cache_blocks(const pa_allocator* a, int32_t* blocks_out, int32_t* depths_out,
+                           int32_t* evictable_out, int32_t cap, int32_t* n_out);
 
 #ifdef __cplusplus
 }

@@ -64,6 +64,11 @@ _SIGS = {
     "pa_batch_append": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp]),
     "pa_export_tables": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_i32, c_vp]),
     "pa_alloc_stats": (c_i32, [c_vp, c_vp]),
+    "pa_alloc_enable_prefix_cache": (c_i32, [c_vp]),
+    "pa_seq_new_cached": (c_i32, [c_vp, c_i64, c_vp, c_i32, c_vp]),
+    "pa_seq_append_tokens": (c_i32, [c_vp, c_i64, c_vp, c_i32, c_vp, c_vp, c_vp]),
+    "pa_prefix_cache_stats": (c_i32, [c_vp, c_vp]),
+    "pa_prefix_cache_blocks": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i32, c_vp]),
 }
 
 
@@ -208,6 +213,49 @@ class BlockAllocator:
               self._L.pa_batch_append(self._h, ptr(seqs), B, ptr(n), ptr(slots), ptr(cow),
                                       ptr(ncow), ptr(tables), int(max_blocks), ptr(lens), ptr(done)))
         return slots[:total], cow[: int(ncow[0])], tables, lens
+
+    # prefix caching
+    def enable_prefix_cache(self) -> int:
+        return self._L.pa_alloc_enable_prefix_cache(self._h)
+
+    def new_cached(self, seq: int, tokens):
+        """Returns (status, cached tokens)."""
+        t = np.ascontiguousarray(tokens, np.int32)
+        out = np.zeros(1, np.int32)
+        rc = self._L.pa_seq_new_cached(self._h, int(seq), ptr(t) if t.size else None, t.size,
+                                       ptr(out))
+        return rc, int(out[0]) if rc == PA_OK else 0
+
+    def append_tokens(self, seq: int, tokens):
+        """Returns (status, slots list, cow pairs list)."""
+        t = np.ascontiguousarray(tokens, np.int32)
+        n = t.size
+        slots = np.zeros(max(n, 1), np.int64)
+        pair = np.zeros(2, np.int32)
+        ncow = np.zeros(1, np.int32)
+        rc = self._L.pa_seq_append_tokens(self._h, int(seq), ptr(t) if n else None, n, ptr(slots),
+                                          ptr(pair), ptr(ncow))
+        if rc != PA_OK:
+            return rc, [], []
+        return rc, slots[:n].tolist(), [(int(pair[0]), int(pair[1]))] if ncow[0] else []
+
+    def prefix_cache_stats(self) -> dict:
+        out = np.zeros(5, np.int64)
+        check("pa_prefix_cache_stats", self._L.pa_prefix_cache_stats(self._h, ptr(out)))
+        return dict(zip(["hit_tokens", "query_tokens", "cached_blocks", "evictable", "evictions"],
+                        out.tolist()))
+
+    def prefix_cache_blocks(self):
+        """({block: depth} of the blocks in the trie, kept blocks in eviction order)."""
+        cap = self.num_blocks
+        b = np.zeros(cap, np.int32)
+        d = np.zeros(cap, np.int32)
+        e = np.full(cap, -1, np.int32)
+        n = np.zeros(1, np.int32)
+        check("pa_prefix_cache_blocks",
+              self._L.pa_prefix_cache_blocks(self._h, ptr(b), ptr(d), ptr(e), cap, ptr(n)))
+        k = self.prefix_cache_stats()["evictable"]
+        return dict(zip(b[: int(n[0])].tolist(), d[: int(n[0])].tolist())), e[:k].tolist()
 
     def export_tables(self, seqs, max_blocks: int):
         seqs = np.ascontiguousarray(seqs, np.int64)

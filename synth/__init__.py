@@ -21,6 +21,7 @@ from .draws import (
     prefill_script,
 )
 from .configs import CONFIGS, config_script
+from .prompts import multi_turn_requests, prefix_kv, prompt_queries
 
 __all__ = [
     "Op",
@@ -34,4 +35,7 @@ __all__ = [
     "prefill_script",
     "CONFIGS",
     "config_script",
+    "multi_turn_requests",
+    "prefix_kv",
+    "prompt_queries",
 ]

@@ -119,3 +119,61 @@ def test_wrong_merge_weight_is_caught(monkeypatch):
         return np.mean(outs, 0)  # forgets the l_p * exp(m_p - M) weights
     monkeypatch.setattr(attention, "decode_partitioned", bad_partitioned)
     _expect_failure(pins.test_partition_merge_equals_one_pass, 3)
+
+
+# ---------------------------------------------------------------- prefix caching
+from tests import test_prefix_cache as tpc
+
+
+def test_most_recent_first_eviction_is_caught(monkeypatch):
+    def bad_kept(self):
+        ks = [b for b in self.cached if self.refcount[b] == 0]
+        return sorted(ks, key=lambda b: (-self.last_use[b], -self.cached[b].depth, b))
+    monkeypatch.setattr(AllocModel, "_kept", bad_kept)
+    _expect_failure(tpc.test_worked_scenario_match_keep_and_evict)
+
+
+def test_matching_the_whole_prompt_is_caught(monkeypatch):
+    def bad_new_cached(self, seq, prompt):
+        # a copy of AllocModel.new_cached that may match every full block,
+        # leaving no prompt token to compute
+        if seq in self.tables:
+            return -4, 0
+        self.clock += 1
+        bs = self.block_size
+        prompt = [int(t) for t in prompt]
+        node, table = self.root, []
+        for i in range(len(prompt) // bs):
+            key = tuple(prompt[i * bs:(i + 1) * bs])
+            if key not in node.children:
+                break
+            node = node.children[key]
+            self.refcount[node.block] += 1
+            self.last_use[node.block] = self.clock
+            table.append(node.block)
+        n_hit = len(table) * bs
+        self.tables[seq], self.lens[seq] = table, n_hit
+        self.tokens[seq], self.walk[seq] = prompt[:n_hit], node
+        self.hit_tokens += n_hit
+        self.query_tokens += len(prompt)
+        return 0, n_hit
+    monkeypatch.setattr(AllocModel, "new_cached", bad_new_cached)
+    _expect_failure(tpc.test_worked_scenario_match_keep_and_evict)
+
+
+def test_freeing_kept_blocks_is_caught(monkeypatch):
+    def bad_release(self, b):
+        self.free.append(b)
+    monkeypatch.setattr(AllocModel, "_release", bad_release)
+    _expect_failure(tpc.test_worked_scenario_match_keep_and_evict)
+
+
+def test_registering_partial_blocks_is_caught(monkeypatch):
+    orig = AllocModel._register
+
+    def bad_register(self, seq, first, last):
+        # also enter the partially filled tail block
+        L = self.lens[seq]
+        return orig(self, seq, first, -(-L // self.block_size) if L % self.block_size else last)
+    monkeypatch.setattr(AllocModel, "_register", bad_register)
+    _expect_failure(tpc.test_worked_scenario_match_keep_and_evict)
