@@ -343,6 +343,88 @@ def bench_prefix_cache(steps: int, warmup: int):
     return res
 
 
+def bench_mixed(steps: int, warmup: int):
+    """Prefill chunks beside decode tokens (32 heads = 32 kv heads, head_dim
+    128): 8 chunks of 512 after 0..3584 cached tokens (multiples of 16) and 192
+    decode tokens with contexts U[512, 2048].  Four ways of running the batch:
+    pa_mixed_step with decode partitions of 256 (one launch + the decode
+    merge) and without (one launch), pa_prefill_chunk on the chunks then
+    pa_decode on the decode tokens (partition 256 + merge), and
+    pa_prefill_chunk on everything (a decode token as a chunk of one).  K/V are random; the block
+    placement is a seeded permutation."""
+    import torch
+
+    from paged_kv_cache_219_amd import BlockAllocator, lib
+    from paged_kv_cache_219_amd.kernels import (decode_workspace, new_kv_cache, pa_decode,
+                                                pa_mixed_step, pa_prefill_chunk)
+
+    H, KVH, D, bs, chunk = 32, 32, 128, 16, 512
+    g = np.random.default_rng(8)
+    cached = (bs * g.integers(0, 3584 // bs, size=8, endpoint=True)).tolist()
+    dlens = g.integers(512, 2048, size=192, endpoint=True).tolist()
+    P, Dn = len(cached), len(dlens)
+    lens_l = [c + chunk for c in cached] + dlens
+    nb = int(np.ceil(1.25 * sum(-(-L // bs) for L in lens_l)))
+    alloc = BlockAllocator(nb, bs, g.permutation(nb).astype(np.int32))
+    for i, L in enumerate(lens_l):
+        alloc.new(i)
+        alloc.append(i, L)
+    mb = max(-(-L // bs) for L in lens_l)
+    tables, lens = alloc.export_tables(list(range(P + Dn)), mb)
+    dev = torch.device("cuda")
+    kc, vc = new_kv_cache(nb, KVH, D, torch.bfloat16, dev)
+    kc.normal_()
+    vc.normal_()
+    bt = torch.from_numpy(tables).to(dev)
+    ln = torch.from_numpy(lens).to(dev)
+    T = P * chunk
+    q = torch.randn((T + Dn, H, D), device=dev).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    qsl_p = torch.tensor(np.arange(P + 1, dtype=np.int32) * chunk, device=dev)
+    qsl_all = torch.tensor(np.concatenate([np.arange(P + 1) * chunk, T + np.arange(1, Dn + 1)])
+                           .astype(np.int32), device=dev)
+    bt_d, ln_d = bt[P:].contiguous(), ln[P:].contiguous()
+    bt_p, ln_p = bt[:P].contiguous(), ln[:P].contiguous()
+    q_d, out_d = q[T:].contiguous(), out[T:].contiguous()
+    ws = decode_workspace(Dn, H, D, max(dlens), 256, dev)
+    ws_m = torch.empty(max(1, lib().pa_mixed_step_workspace_bytes(Dn, H, D, max(dlens), 256)),
+                       dtype=torch.uint8, device=dev)
+    scale = float(np.float32(1 / np.sqrt(D)))
+    runs = {
+        "mixed": lambda: pa_mixed_step(out, q, kc, vc, bt, qsl_p, ln, T, chunk, max(dlens), scale,
+                                       256, ws_m),
+        "mixed_unsplit": lambda: pa_mixed_step(out, q, kc, vc, bt, qsl_p, ln, T, chunk, max(dlens),
+                                               scale, 0),
+        "split": lambda: (pa_prefill_chunk(out, q, kc, vc, bt_p, qsl_p, ln_p, chunk, scale),
+                          pa_decode(out_d, q_d, kc, vc, bt_d, ln_d, scale, 256, max(dlens), ws)),
+        "as_prefill": lambda: pa_prefill_chunk(out, q, kc, vc, bt, qsl_all, ln, chunk, scale),
+    }
+    stream = torch.cuda.current_stream(dev)
+    res = {"workload": "mixed_step_bf16", "prefill_seqs": P, "chunk": chunk, "decode_seqs": Dn,
+           "heads": H, "kv_heads": KVH, "head_dim": D}
+    for name, fn in runs.items():
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for it in range(warmup + steps):
+            if it >= warmup:
+                ev[it - warmup][0].record(stream)
+            fn()
+            if it >= warmup:
+                ev[it - warmup][1].record(stream)
+        torch.cuda.synchronize()
+        res[f"{name}_ms"] = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    flops = prefill_flops(cached, [chunk] * P, SimpleNamespace(head_dim=D, num_heads=H))
+    dbytes = sum(dlens) * KVH * D * 2 * 2
+    res["prefill_flops"] = flops
+    res["decode_kv_bytes"] = dbytes
+    # both resources busy at once at best: the slower of the two at peak
+    res["roofline_ms"] = max(flops / (BF16_PEAK_TFLOPS * 1e12), dbytes / (HBM_PEAK_GBS * 1e9)) * 1e3
+    res["mixed_roofline_frac"] = res["roofline_ms"] / res["mixed_ms"]
+    del kc, vc
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(budget_s: float = 10.0, max_passes: int = 8):
     """The fp64 numpy oracle decoding the headline workload's batch, four
     sequences at a time, single-threaded (BLAS pinned to one thread).  The
@@ -516,6 +598,8 @@ def run_workload(spec: str, steps: int, warmup: int):
         raise SystemExit(f"unknown workload mode {mode!r}")
     if name == "prefix_cache_multi_turn_bf16":
         return bench_prefix_cache(steps, warmup)
+    if name == "mixed_step_bf16":
+        return bench_mixed(steps, warmup)
     if "prefill" in name:
         return bench_prefill(name, steps, warmup)
     return bench_decode(name, steps, warmup, grouped=mode == "grouped")
@@ -528,7 +612,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--configs",
                     default="gqa_decode_bf16,shared_prefix_bf16,shared_prefix_bf16:grouped,"
-                            "chunked_prefill_bf16,prefix_cache_multi_turn_bf16",
+                            "chunked_prefill_bf16,prefix_cache_multi_turn_bf16,mixed_step_bf16",
                     help="extra workloads reported under 'workloads' ('' for none); a decode "
                          "workload suffixed ':grouped' runs through pa_decode_shared_prefix")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -566,6 +650,11 @@ def main():
                   f"{r['host_us_per_request']:.1f} us/request on the host; last-turn prefill "
                   f"{r['cached_prefill_ms']:.3f} ms cached vs {r['recompute_prefill_ms']:.3f} ms "
                   f"recomputed", file=sys.stderr, flush=True)
+        elif name == "mixed_step_bf16":
+            print(f"[bench] {name}: mixed {r['mixed_ms']:.3f} ms (unsplit decode "
+                  f"{r['mixed_unsplit_ms']:.3f}), prefill + decode "
+                  f"{r['split_ms']:.3f} ms, all as chunks {r['as_prefill_ms']:.3f} ms "
+                  f"(roofline {r['roofline_ms']:.3f} ms)", file=sys.stderr, flush=True)
         elif "prefill" in name:
             print(f"[bench] {name}: {r['prefill_ms']:.3f} ms = {r['prefill_TFLOPs']:.1f} TFLOP/s",
                   file=sys.stderr, flush=True)

@@ -266,6 +266,55 @@ int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* 
                      int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
                      int32_t dtype, void* stream);
 
+/*
+ * pa_mixed_step -- one launch for a batch that mixes prefill chunks and
+ * single decode tokens (deep-dive page, sections "Chunked Prefill" and "Cơ chế
+ * của Chunked Prefill": the scheduler interleaves prefill chunks with other
+ * requests' decode steps; the tr.news.hada.io summary page: requests join
+ * the batch as they arrive and finished ones leave it).
+ *
+ * Sequences 0 .. num_prefill_seqs-1 are chunks, exactly as in
+ * pa_prefill_chunk (query rows query_start_loc[s] .. query_start_loc[s+1]-1,
+ * query_start_loc[num_prefill_seqs] == num_prefill_tokens).  Sequences
+ * num_prefill_seqs .. num_prefill_seqs+num_decode_seqs-1 are decode steps, as
+ * in pa_decode: decode sequence j has the one query row num_prefill_tokens + j
+ * and attends to its whole context.
+ *
+ *   out, q           device bf16 [num_prefill_tokens + num_decode_seqs]
+ *                    [num_heads][head_dim].
+ *   block_tables     device int32 [num_prefill_seqs + num_decode_seqs]
+ *                    [max_blocks_per_seq]; context_lens likewise [..].
+ *   query_start_loc  device int32 [num_prefill_seqs + 1] (may be NULL when
+ *                    num_prefill_seqs == 0).
+ *   max_query_len    host upper bound of the chunks' n_q.
+ *   max_decode_context  host upper bound of the decode sequences' contexts
+ *                    (sizes the grid); with partition 0, a decode sequence
+ *                    whose context exceeds it gets no output.
+ *   partition        decode partition in tokens, as in pa_decode: 0 = one
+ *                    partition covering max_decode_context, else a positive
+ *                    multiple of 64; decode sequences longer than one
+ *                    partition are merged by a second launch.
+ *   workspace        device scratch of pa_mixed_step_workspace_bytes(...)
+ *                    bytes (NULL when that is 0), as in pa_decode.
+ * Prefill rows are computed by the pa_prefill_chunk workgroup (bit-identical
+ * to it), decode rows by the one-wave decode body (bit-identical to pa_decode
+ * with the same partition when num_heads / num_kv_heads is 1 or 2).  bf16,
+ * head_dim 128, num_heads / num_kv_heads in {1, 2, 4, 8}.
+ */
+int pa_mixed_step(void* out, const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                  const int32_t* query_start_loc, const int32_t* context_lens,
+                  int32_t num_prefill_seqs, int32_t num_prefill_tokens, int32_t max_query_len,
+                  int32_t num_decode_seqs, int32_t max_decode_context, int32_t num_heads,
+                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                  float scale, int32_t partition, void* workspace, size_t workspace_bytes,
+                  int32_t dtype, void* stream);
+
+/* Workspace bytes of pa_mixed_step: the decode partials, as in pa_decode. */
+size_t pa_mixed_step_workspace_bytes(int32_t num_decode_seqs, int32_t num_heads,
+                                     int32_t head_dim, int32_t max_decode_context,
+                                     int32_t partition);
+
 /* ---------------------------------------------------------- block allocator */
 
 /*

@@ -50,6 +50,10 @@ _SIGS = {
                                         c_i32, c_vp, c_i32, c_vp, c_sz, c_i32, c_vp]),
     "pa_prefill_chunk": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32,
                                  c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp]),
+    "pa_mixed_step": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32,
+                              c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp,
+                              c_sz, c_i32, c_vp]),
+    "pa_mixed_step_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_alloc_create": (c_i32, [c_i32, c_i32, c_vp, ctypes.POINTER(c_vp)]),
     "pa_alloc_destroy": (None, [c_vp]),
     "pa_seq_new": (c_i32, [c_vp, c_i64]),

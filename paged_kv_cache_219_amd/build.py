@@ -24,7 +24,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["allocator.cpp", "prefix_plan.cpp", "cache_ops.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["allocator.cpp", "prefix_plan.cpp", "cache_ops.hip", "decode.hip", "prefill.hip",
+           "mixed.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
@@ -33,11 +34,12 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
           "-munsafe-fp-atomics"]
 
 
-# Per-source extras.  The prefill kernel never lets a NaN reach arithmetic
-# that matters (masked scores are replaced by -inf with a select, tail values
-# are zeroed bitwise), so it is built assuming no NaN operands: fmax then needs
-# no canonicalising instruction per operand.
-EXTRA = {"prefill.hip": ["-fno-honor-nans"]}
+# Per-source extras.  The prefill and decode bodies never let a NaN reach
+# arithmetic that matters (masked scores are replaced by -inf with a select,
+# tail values are zeroed bitwise), so the matrix-core sources are built
+# assuming no NaN operands: fmax then needs no canonicalising instruction per
+# operand.
+EXTRA = {"prefill.hip": ["-fno-honor-nans"], "mixed.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:

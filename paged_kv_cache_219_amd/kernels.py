@@ -255,3 +255,48 @@ def pa_prefill_chunk(out, q, k_cache, v_cache, block_tables, query_start_loc, co
         block_tables.data_ptr(), block_tables.shape[1], query_start_loc.data_ptr(),
         context_lens.data_ptr(), B, int(max_query_len), H, kvh, d, bs, nb, float(scale),
         _dtype(q), _stream(q)))
+
+
+def pa_mixed_step(out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens,
+                  num_prefill_tokens: int, max_query_len: int, max_decode_context: int,
+                  scale: float, partition: int = 0, workspace=None, check_device_args=False):
+    """Prefill chunks (the first len(query_start_loc) - 1 sequences) and decode
+    tokens (the rest, one query row each, after the chunks' rows) in one
+    launch (plus the decode merge when partitioned)."""
+    nb, kvh, d, bs = _cache_dims(k_cache, v_cache)
+    T, H = q.shape[0], q.shape[1]
+    B = context_lens.shape[0]
+    P = query_start_loc.shape[0] - 1
+    Dn = B - P
+    if P < 0 or Dn < 0 or T != num_prefill_tokens + Dn:
+        raise ValueError("q rows must be the chunks' rows followed by one row per decode sequence")
+    if q.shape != (T, H, d) or out.shape != q.shape or not (q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("q/out must be contiguous [T, H, head_dim]")
+    if q.dtype != k_cache.dtype or out.dtype != q.dtype:
+        raise TypeError("q/out dtype must match the cache")
+    if query_start_loc.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("query_start_loc and context_lens must be int32")
+    if block_tables.dtype != torch.int32 or block_tables.shape[0] != B or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be contiguous int32 [B, max_blocks]")
+    if check_device_args:
+        _check_tables(block_tables, context_lens, nb, bs)
+        qsl = query_start_loc.cpu().numpy()
+        lens = context_lens.cpu().numpy()
+        nq = np.diff(qsl)
+        if qsl[0] != 0 or qsl[-1] != num_prefill_tokens or (nq < 0).any() \
+                or (nq > max_query_len).any() or (nq > lens[:P]).any():
+            raise ValueError("query_start_loc inconsistent with the chunks")
+        if Dn and (lens[P:].max() > max_decode_context or lens[P:].min() < 0):
+            raise ValueError("a decode context exceeds max_decode_context")
+    need = int(lib().pa_mixed_step_workspace_bytes(Dn, H, d, int(max_decode_context),
+                                                   int(partition)))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    check("pa_mixed_step", lib().pa_mixed_step(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_tables.data_ptr(), block_tables.shape[1],
+        query_start_loc.data_ptr() if P else None, context_lens.data_ptr(), P,
+        int(num_prefill_tokens), int(max_query_len), Dn, int(max_decode_context), H, kvh, d, bs,
+        nb, float(scale), int(partition), wptr, wbytes, _dtype(q), _stream(q)))

@@ -19,6 +19,7 @@ from .draws import (
     decode_script,
     shared_prefix_script,
     prefill_script,
+    mixed_script,
 )
 from .configs import CONFIGS, config_script
 from .prompts import multi_turn_requests, prefix_kv, prompt_queries
@@ -33,6 +34,7 @@ __all__ = [
     "decode_script",
     "shared_prefix_script",
     "prefill_script",
+    "mixed_script",
     "CONFIGS",
     "config_script",
     "multi_turn_requests",

@@ -248,3 +248,39 @@ def prefill_script(spec: Spec, cached: Sequence[int], chunk: int, seed: int,
     mb = _ceil_div(max(lens), bs)
     return Script(spec, seed, nb, placement(seed, nb), setup, step, list(range(len(cached))),
                   [chunk] * len(cached), mb, {"context_lens": lens, "cached": cached})
+
+
+def mixed_script(spec: Spec, cached: Sequence[int], chunk: int, decode_lens: Sequence[int],
+                 seed: int, pool_factor: float = 1.25) -> Script:
+    """A batch mixing prefill chunks and decode tokens.
+
+    Sequences 0 .. len(cached)-1 hold ``cached[i]`` tokens and the step
+    appends a chunk of ``chunk`` tokens (its query rows); sequences after them
+    hold ``decode_lens[j] - 1`` tokens and the step appends one token (one
+    query row).  ``spec.kind`` is "prefill": a decode token is a chunk of
+    one."""
+    bs = spec.block_size
+    cached = [int(x) for x in cached]
+    decode_lens = [int(x) for x in decode_lens]
+    P = len(cached)
+    needed = (sum(_ceil_div(c + chunk, bs) for c in cached)
+              + sum(_ceil_div(L, bs) for L in decode_lens))
+    nb = _pool(needed, pool_factor)
+    setup: List[Op] = []
+    step: List[Op] = []
+    j = 0
+    hist = cached + [L - 1 for L in decode_lens]
+    for i, c in enumerate(hist):
+        setup.append(Op("new", i))
+        if c > 0:
+            setup.append(Op("append", i, n=c, stream=STREAM_APPEND0 + j))
+            j += 1
+    qlens = [chunk] * P + [1] * len(decode_lens)
+    for i, n in enumerate(qlens):
+        step.append(Op("append", i, n=n, stream=STREAM_APPEND0 + j))
+        j += 1
+    lens = [c + chunk for c in cached] + decode_lens
+    mb = _ceil_div(max(lens), bs)
+    return Script(spec, seed, nb, placement(seed, nb), setup, step, list(range(len(lens))),
+                  qlens, mb, {"context_lens": lens, "cached": cached, "num_prefill": P,
+                              "chunk": chunk})

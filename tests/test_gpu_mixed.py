@@ -1,0 +1,86 @@
+"""GPU parity of the mixed prefill + decode launch (pa_mixed_step).
+
+One batch holds prefill chunks (ragged, after 0 to 513 cached tokens) and
+decode tokens (contexts 1 to 2047): every output row must match the oracle's
+causal attention for its position (a decode token is a chunk of one).  The
+chunk rows must also be bit-identical to pa_prefill_chunk, and for groups of
+1 or 2 query heads per kv head the decode rows bit-identical to pa_decode
+without partitions: the launch runs the same workgroup bodies.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_219_amd.kernels import pa_decode, pa_mixed_step, pa_prefill_chunk
+from paged_kv_cache_219_amd.workload import DeviceWorkload, to_host_bits
+from synth import Spec, mixed_script
+
+from .parity import assert_close, oracle_step, say
+
+pytestmark = pytest.mark.gpu
+
+DECODE_LENS = [1, 2, 16, 17, 64, 65, 300, 1000, 2047]
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("a GPU test ran without a GPU")
+
+
+def _run(H, KVH, cached, chunk, decode_lens, seed=41, partition=0):
+    spec = Spec(f"mixed_{H}_{KVH}", "prefill", H, KVH, 128, 16, "bf16")
+    sc = mixed_script(spec, cached, chunk, decode_lens, seed)
+    w = DeviceWorkload(sc)
+    w.run_step()
+    bt, lens, _, lens_h = w.batch_tables()
+    q = w.queries(0)
+    P, Dn = len(cached), len(decode_lens)
+    qsl = torch.tensor(np.concatenate([[0], np.cumsum([chunk] * P)]).astype(np.int32),
+                       device="cuda")
+    out = torch.empty_like(q)
+    pa_mixed_step(out, q, w.k_cache, w.v_cache, bt, qsl, lens, P * chunk, chunk if P else 0,
+                  max(decode_lens) if Dn else 0, spec.scale, partition=partition,
+                  check_device_args=True)
+    torch.cuda.synchronize()
+    return sc, w, bt, lens, q, out
+
+
+@pytest.mark.parametrize("partition", [0, 256])
+@pytest.mark.parametrize("H,KVH", [(4, 4), (8, 4), (8, 2), (16, 2)])
+def test_mixed_batch_matches_oracle_and_the_separate_launches(H, KVH, partition):
+    cached, chunk = [0, 48, 100, 513], 70
+    say(f"mixed step H={H} KVH={KVH} partition={partition}: {len(cached)} chunks of {chunk} + "
+        f"{len(DECODE_LENS)} decode")
+    sc, w, bt, lens, q, out = _run(H, KVH, cached, chunk, DECODE_LENS, partition=partition)
+    st, ref = oracle_step(sc)
+    mx, rel = assert_close(out, ref, "bf16", what="mixed step")
+    say(f"  max abs {mx:.2e} rel L2 {rel:.2e}")
+    P, T = len(cached), len(cached) * chunk
+    # chunk rows: the prefill workgroup, bit for bit
+    qsl_all = torch.tensor(np.concatenate([[0], np.cumsum(sc.query_lens)]).astype(np.int32),
+                           device="cuda")
+    out_pf = torch.empty_like(q)
+    pa_prefill_chunk(out_pf, q, w.k_cache, w.v_cache, bt, qsl_all, lens, chunk, sc.spec.scale)
+    # decode rows: the one-wave decode body, bit for bit where pa_decode uses it
+    out_dec = torch.empty_like(q[T:])
+    pa_decode(out_dec, q[T:].contiguous(), w.k_cache, w.v_cache, bt[P:].contiguous(),
+              lens[P:].contiguous(), sc.spec.scale, partition, max(DECODE_LENS))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host_bits(out[:T]), to_host_bits(out_pf[:T]))
+    if H // KVH <= 2:
+        assert np.array_equal(to_host_bits(out[T:]), to_host_bits(out_dec))
+    else:
+        assert_close(out_dec, ref[T:], "bf16", what="pa_decode rows")
+
+
+@pytest.mark.parametrize("kind", ["decode_only", "prefill_only"])
+def test_mixed_batch_with_one_kind_only(kind):
+    say(f"mixed step, {kind}")
+    if kind == "decode_only":
+        sc, w, bt, lens, q, out = _run(8, 8, [], 1, DECODE_LENS, partition=128)
+    else:
+        sc, w, bt, lens, q, out = _run(8, 8, [0, 32, 5], 129, [])
+    st, ref = oracle_step(sc)
+    assert_close(out, ref, "bf16", what=kind)
