@@ -425,6 +425,67 @@ def bench_mixed(steps: int, warmup: int):
     return res
 
 
+def bench_block_sizes(steps: int, warmup: int):
+    """pa_decode on the headline shape (batch 64, 32 heads = 32 kv heads,
+    head_dim 128, contexts U[512, 2048], partition 256) at block sizes 8, 16,
+    32 and 64, each with the pool's blocks handed out in a seeded random order
+    (pages scattered) and in index order (every sequence's blocks
+    consecutive, as in a contiguous cache).  Reports decode GB/s of KV bytes
+    and the internal fragmentation the block size costs (slots allocated but
+    unused: below one block per sequence)."""
+    import torch
+
+    from paged_kv_cache_219_amd import BlockAllocator
+    from paged_kv_cache_219_amd.kernels import decode_workspace, new_kv_cache, pa_decode
+
+    H, D, B, part = 32, 128, 64, 256
+    g = np.random.default_rng(2)
+    lens_l = g.integers(512, 2048, size=B, endpoint=True).tolist()
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream(dev)
+    q = torch.randn((B, H, D), device=dev).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    scale = float(np.float32(1 / np.sqrt(D)))
+    kvb = sum(lens_l) * H * D * 2 * 2
+    rows = []
+    for bs in (8, 16, 32, 64):
+        needed = sum(-(-L // bs) for L in lens_l)
+        nb = int(np.ceil(1.25 * needed))
+        kc, vc = new_kv_cache(nb, H, D, torch.bfloat16, dev, bs)
+        kc.normal_()
+        vc.normal_()
+        for placement in ("random", "contiguous"):
+            order = (g.permutation(nb) if placement == "random" else np.arange(nb)).astype(np.int32)
+            alloc = BlockAllocator(nb, bs, order)
+            for i, L in enumerate(lens_l):
+                alloc.new(i)
+                alloc.append(i, L)
+            waste = alloc.stats()["wasted_slots"]
+            mb = max(-(-L // bs) for L in lens_l)
+            tables, lens = alloc.export_tables(list(range(B)), mb)
+            bt = torch.from_numpy(tables).to(dev)
+            ln = torch.from_numpy(lens).to(dev)
+            ws = decode_workspace(B, H, D, max(lens_l), part, dev)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)]
+            for it in range(warmup + steps):
+                if it >= warmup:
+                    ev[it - warmup][0].record(stream)
+                pa_decode(out, q, kc, vc, bt, ln, scale, part, max(lens_l), ws)
+                if it >= warmup:
+                    ev[it - warmup][1].record(stream)
+            torch.cuda.synchronize()
+            ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+            rows.append({"block_size": bs, "placement": placement, "decode_ms": ms,
+                         "decode_kv_GBs": kvb / (ms * 1e-3) / 1e9,
+                         "wasted_slots": waste, "wasted_frac": waste / (needed * bs),
+                         "table_entries": needed})
+        del kc, vc
+        torch.cuda.empty_cache()
+    return {"workload": "block_size_sweep_bf16", "batch": B, "heads": H, "head_dim": D,
+            "partition": part, "kv_bytes": kvb, "rows": rows}
+
+
 def cpu_baseline(budget_s: float = 10.0, max_passes: int = 8):
     """The fp64 numpy oracle decoding the headline workload's batch, four
     sequences at a time, single-threaded (BLAS pinned to one thread).  The
@@ -490,7 +551,10 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
 # counter run cannot time the kernel); the figure is used only while the
 # kernel sources still hash to what was profiled.
 
-DECODE_SOURCES = ("paged_kv_cache_219_amd/csrc/decode.hip", "paged_kv_cache_219_amd/csrc/pa_device.h")
+DECODE_SOURCES = ("paged_kv_cache_219_amd/csrc/decode.hip",
+                  "paged_kv_cache_219_amd/csrc/decode_core.h",
+                  "paged_kv_cache_219_amd/csrc/page_ring.h",
+                  "paged_kv_cache_219_amd/csrc/pa_device.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pa_decode.decode_bf16.traffic.txt")
 CALIB_BYTES = 1 << 30  # copy_calibration's read (and write) size
 
@@ -600,6 +664,8 @@ def run_workload(spec: str, steps: int, warmup: int):
         return bench_prefix_cache(steps, warmup)
     if name == "mixed_step_bf16":
         return bench_mixed(steps, warmup)
+    if name == "block_size_sweep_bf16":
+        return bench_block_sizes(steps, warmup)
     if "prefill" in name:
         return bench_prefill(name, steps, warmup)
     return bench_decode(name, steps, warmup, grouped=mode == "grouped")
@@ -612,7 +678,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--configs",
                     default="gqa_decode_bf16,shared_prefix_bf16,shared_prefix_bf16:grouped,"
-                            "chunked_prefill_bf16,prefix_cache_multi_turn_bf16,mixed_step_bf16",
+                            "chunked_prefill_bf16,prefix_cache_multi_turn_bf16,mixed_step_bf16,"
+                            "block_size_sweep_bf16",
                     help="extra workloads reported under 'workloads' ('' for none); a decode "
                          "workload suffixed ':grouped' runs through pa_decode_shared_prefix")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -650,6 +717,10 @@ def main():
                   f"{r['host_us_per_request']:.1f} us/request on the host; last-turn prefill "
                   f"{r['cached_prefill_ms']:.3f} ms cached vs {r['recompute_prefill_ms']:.3f} ms "
                   f"recomputed", file=sys.stderr, flush=True)
+        elif name == "block_size_sweep_bf16":
+            print(f"[bench] {name}: " + ", ".join(
+                f"bs{x['block_size']}/{x['placement'][:4]} {x['decode_kv_GBs']:.0f} GB/s"
+                for x in r["rows"]), file=sys.stderr, flush=True)
         elif name == "mixed_step_bf16":
             print(f"[bench] {name}: mixed {r['mixed_ms']:.3f} ms (unsplit decode "
                   f"{r['mixed_unsplit_ms']:.3f}), prefill + decode "

@@ -28,8 +28,10 @@
  *  - dtype: PA_F32 (float) or PA_BF16 (bfloat16 stored as raw 16-bit).
  *    Outputs have the dtype of the inputs; accumulation is fp32 and the final
  *    bf16 rounding is round-to-nearest-even.
- *  - block_size is 16 (the value every example on the deep-dive page uses);
- *    head_dim is 64 or 128.  Anything else returns PA_ERR_UNSUPPORTED.
+ *  - block_size is 16, the value every example on the deep-dive page uses;
+ *    pa_reshape_and_cache, pa_copy_blocks and pa_decode also take 8, 32 and
+ *    64 (the page's block_size trade-off).  head_dim is 64 or 128.  Anything
+ *    else returns PA_ERR_UNSUPPORTED.
  *
  * Cache layout (the pages leave it open).  X = 16 / sizeof(element)
  * (8 for bf16, 4 for fp32):

@@ -117,7 +117,8 @@ extern "C" int pa_reshape_and_cache(const void* key, const void* value, void* k_
   if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
     return PA_ERR_INVALID_ARG;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
-  if (block_size != 16) return PA_ERR_UNSUPPORTED;
+  if (block_size != 8 && block_size != 16 && block_size != 32 && block_size != 64)
+    return PA_ERR_UNSUPPORTED;
   const int64_t row = static_cast<int64_t>(num_kv_heads) * head_dim;
   if (key_stride < row || value_stride < row) return PA_ERR_INVALID_ARG;
   if (num_tokens == 0) return PA_OK;
@@ -154,7 +155,8 @@ extern "C" int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs
   if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
     return PA_ERR_INVALID_ARG;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
-  if (block_size != 16) return PA_ERR_UNSUPPORTED;
+  if (block_size != 8 && block_size != 16 && block_size != 32 && block_size != 64)
+    return PA_ERR_UNSUPPORTED;
   if (num_pairs == 0) return PA_OK;
   if (!k_cache || !v_cache || !pairs) return PA_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache)) & 15)

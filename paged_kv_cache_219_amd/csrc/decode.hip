@@ -7,7 +7,7 @@
 namespace {
 
 // One wave (one 64-thread workgroup) per item.
-template <typename T, int D, int G, bool PVB>
+template <typename T, int D, int G, bool PVB, int BS>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(
     T* __restrict__ out, Partials ws, const T* __restrict__ q, const T* __restrict__ kc,
     const T* __restrict__ vc, const int32_t* __restrict__ block_tables, int32_t max_blocks,
@@ -15,9 +15,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     int32_t num_kv_heads, int32_t num_parts, int32_t partition, float scale_log2,
     RangeSplit rs) {
   __shared__ __attribute__((aligned(16))) weight_t<PVB> p_lds[G * kTile];
-  decode_item<T, D, G, PVB>(blockIdx.x, p_lds, out, ws, q, kc, vc, block_tables, max_blocks,
-                            context_lens, num_seqs, num_heads, num_kv_heads, num_parts, partition,
-                            scale_log2, rs);
+  decode_item<T, D, G, PVB, BS>(blockIdx.x, p_lds, out, ws, q, kc, vc, block_tables,
+                                max_blocks, context_lens, num_seqs, num_heads, num_kv_heads,
+                                num_parts, partition, scale_log2, rs);
 }
 
 // Grouped-query decode (4 or 8 query heads per kv head; bf16, head_dim 128).
@@ -354,13 +354,13 @@ struct Split {
   RangeSplit rs;
 };
 
-template <typename T, int D, int G, bool PVB>
+template <typename T, int D, int G, bool PVB, int BS>
 int launch_decode(void* out, const void* q, const void* kc, const void* vc, const int32_t* bt,
                   int32_t max_blocks, const int32_t* lens, int32_t B, int32_t H, int32_t KVH,
                   Split sp, int32_t partition, float scale_log2, void* ws, hipStream_t st) {
   const Partials p = carve(ws, B, H, D, sp.slots);
   const int64_t grid = static_cast<int64_t>(sp.parts) * KVH * B;
-  if constexpr (sizeof(T) == 2 && D == 128 && (G == 4 || G == 8)) {
+  if constexpr (BS == kBS && sizeof(T) == 2 && D == 128 && (G == 4 || G == 8)) {
     constexpr int W = G == 8 ? kGroupWaves8 : 4;
     hipLaunchKernelGGL((decode_group_kernel<G / W, W>), dim3(static_cast<uint32_t>(grid)),
                        dim3(W * 64), 0, st, static_cast<uint16_t*>(out), p,
@@ -368,7 +368,7 @@ int launch_decode(void* out, const void* q, const void* kc, const void* vc, cons
                        static_cast<const uint16_t*>(vc), bt, max_blocks, lens, B, H, KVH, sp.slots,
                        partition, scale_log2, sp.rs);
   } else {
-    hipLaunchKernelGGL((decode_kernel<T, D, G, PVB>), dim3(static_cast<uint32_t>(grid)), dim3(64),
+    hipLaunchKernelGGL((decode_kernel<T, D, G, PVB, BS>), dim3(static_cast<uint32_t>(grid)), dim3(64),
                        0, st, static_cast<T*>(out), p, static_cast<const T*>(q),
                        static_cast<const T*>(kc), static_cast<const T*>(vc), bt, max_blocks, lens,
                        B, H, KVH, sp.slots, partition, scale_log2, sp.rs);
@@ -379,19 +379,35 @@ int launch_decode(void* out, const void* q, const void* kc, const void* vc, cons
   return pa_launch_status();
 }
 
-template <typename T, int D>
+template <typename T, int D, int BS = kBS>
 int dispatch_group(int G, void* out, const void* q, const void* kc, const void* vc,
                    const int32_t* bt, int32_t mb, const int32_t* lens, int32_t B, int32_t H,
                    int32_t KVH, Split sp, int32_t partition, float sl2, void* ws,
                    hipStream_t st) {
   constexpr bool kBf = sizeof(T) == 2;
   switch (G) {
-    case 1: return launch_decode<T, D, 1, false>(out, q, kc, vc, bt, mb, lens, B, H, KVH, sp, partition, sl2, ws, st);
-    case 2: return launch_decode<T, D, 2, false>(out, q, kc, vc, bt, mb, lens, B, H, KVH, sp, partition, sl2, ws, st);
-    case 4: return launch_decode<T, D, 4, kBf>(out, q, kc, vc, bt, mb, lens, B, H, KVH, sp, partition, sl2, ws, st);
-    case 8: return launch_decode<T, D, 8, kBf>(out, q, kc, vc, bt, mb, lens, B, H, KVH, sp, partition, sl2, ws, st);
+    case 1: return launch_decode<T, D, 1, false, BS>(out, q, kc, vc, bt, mb, lens, B, H, KVH, sp, partition, sl2, ws, st);
+    case 2: return launch_decode<T, D, 2, false, BS>(out, q, kc, vc, bt, mb, lens, B, H, KVH, sp, partition, sl2, ws, st);
+    case 4: return launch_decode<T, D, 4, kBf, BS>(out, q, kc, vc, bt, mb, lens, B, H, KVH, sp, partition, sl2, ws, st);
+    case 8: return launch_decode<T, D, 8, kBf, BS>(out, q, kc, vc, bt, mb, lens, B, H, KVH, sp, partition, sl2, ws, st);
     default: return PA_ERR_UNSUPPORTED;
   }
+}
+
+// dtype and head_dim dispatch for one block size
+template <int BS>
+int dispatch_block(int32_t dtype, int32_t head_dim, int G, void* out, const void* q,
+                   const void* kc, const void* vc, const int32_t* bt, int32_t mb,
+                   const int32_t* lens, int32_t B, int32_t H, int32_t KVH, Split sp,
+                   int32_t partition, float sl2, void* ws, hipStream_t st) {
+  if (dtype == PA_BF16) {
+    if (head_dim == 128)
+      return dispatch_group<uint16_t, 128, BS>(G, out, q, kc, vc, bt, mb, lens, B, H, KVH, sp, partition, sl2, ws, st);
+    return dispatch_group<uint16_t, 64, BS>(G, out, q, kc, vc, bt, mb, lens, B, H, KVH, sp, partition, sl2, ws, st);
+  }
+  if (head_dim == 128)
+    return dispatch_group<float, 128, BS>(G, out, q, kc, vc, bt, mb, lens, B, H, KVH, sp, partition, sl2, ws, st);
+  return dispatch_group<float, 64, BS>(G, out, q, kc, vc, bt, mb, lens, B, H, KVH, sp, partition, sl2, ws, st);
 }
 
 
@@ -415,9 +431,11 @@ extern "C" int pa_decode(void* out, const void* q, const void* k_cache, const vo
       num_blocks <= 0 || partition < 0 || max_context_len < 0)
     return PA_ERR_INVALID_ARG;
   if (num_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
-  if (block_size != kBS || (head_dim != 64 && head_dim != 128)) return PA_ERR_UNSUPPORTED;
+  if ((block_size != 8 && block_size != 16 && block_size != 32 && block_size != 64) ||
+      (head_dim != 64 && head_dim != 128))
+    return PA_ERR_UNSUPPORTED;
   if (partition % kTile != 0) return PA_ERR_INVALID_ARG;
-  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * kBS)
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
     return PA_ERR_INVALID_ARG;
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
@@ -439,14 +457,17 @@ extern "C" int pa_decode(void* out, const void* q, const void* k_cache, const vo
   const float sl2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const Split sp{static_cast<int32_t>(parts), static_cast<int32_t>(parts), {nullptr, 0, part}};
-  if (dtype == PA_BF16) {
-    if (head_dim == 128)
-      return dispatch_group<uint16_t, 128>(G, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads, num_kv_heads, sp, part, sl2, workspace, st);
-    return dispatch_group<uint16_t, 64>(G, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads, num_kv_heads, sp, part, sl2, workspace, st);
+#define PA_DECODE_BS(BSZ)                                                                      \
+  dispatch_block<BSZ>(dtype, head_dim, G, out, q, k_cache, v_cache, block_tables,              \
+                      max_blocks_per_seq, context_lens, num_seqs, num_heads, num_kv_heads, sp, \
+                      part, sl2, workspace, st)
+  switch (block_size) {
+    case 8: return PA_DECODE_BS(8);
+    case 32: return PA_DECODE_BS(32);
+    case 64: return PA_DECODE_BS(64);
+    default: return PA_DECODE_BS(16);
   }
-  if (head_dim == 128)
-    return dispatch_group<float, 128>(G, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads, num_kv_heads, sp, part, sl2, workspace, st);
-  return dispatch_group<float, 64>(G, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads, num_kv_heads, sp, part, sl2, workspace, st);
+#undef PA_DECODE_BS
 }
 
 namespace {

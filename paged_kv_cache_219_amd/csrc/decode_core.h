@@ -54,15 +54,19 @@ __device__ __forceinline__ void lds_wave_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-template <typename T, int D>
+// Shapes of the one-wave decode for element type T, head_dim D and block size
+// BS (8, 16, 32 or 64 tokens; a 64-token tile is NP pages).
+template <typename T, int D, int BS = kBS>
 struct Geo {
+  static_assert(BS == 8 || BS == 16 || BS == 32 || BS == 64, "block size 8, 16, 32 or 64");
   static constexpr int E = sizeof(T);
   static constexpr int X = 16 / E;          // elements per 16-byte chunk
   static constexpr int NKC = D / X;         // key chunks per token row
-  static constexpr int LPR = kBS / X;       // lanes per value d-row (one row = 16 tokens)
+  static constexpr int NP = 64 / BS;        // pages per 64-token tile
+  static constexpr int LPR = BS / X;        // lanes per value d-row (one row = BS tokens), <= 16
   static constexpr int DPI = 64 / LPR;      // value d-rows covered by one wave load
   static constexpr int NVI = D / DPI;       // wave loads per value page
-  static constexpr int PAGE = D * kBS;      // elements per (block, kv head) page
+  static constexpr int PAGE = D * BS;       // elements per (block, kv head) page
 };
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -130,7 +134,7 @@ using weight_t = typename std::conditional<PVB, uint16_t, float>::type;
 
 // One item (partition, sequence, kv head) of the one-wave decode, run by one
 // wave of the calling workgroup; p_lds is that wave's own G * 64 weights.
-template <typename T, int D, int G, bool PVB>
+template <typename T, int D, int G, bool PVB, int BS = kBS>
 __device__ __forceinline__ void decode_item(
     uint32_t li, weight_t<PVB>* __restrict__ p_lds, T* __restrict__ out, Partials ws,
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
@@ -138,8 +142,9 @@ __device__ __forceinline__ void decode_item(
     const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t num_heads,
     int32_t num_kv_heads, int32_t num_parts, int32_t partition, float scale_log2,
     RangeSplit rs) {
-  using Gm = Geo<T, D>;
+  using Gm = Geo<T, D, BS>;
   constexpr int X = Gm::X, NKC = Gm::NKC, LPR = Gm::LPR, DPI = Gm::DPI, NVI = Gm::NVI;
+  constexpr int NP = Gm::NP;
   typedef weight_t<PVB> p_t;
 
   // Logical order (partition, sequence, kv head), kv head fastest, in plain
@@ -190,17 +195,17 @@ __device__ __forceinline__ void decode_item(
   const int32_t* bt_row = block_tables + static_cast<int64_t>(s) * max_blocks;
   const int64_t head_off = static_cast<int64_t>(g) * Gm::PAGE;
   const int64_t blk_stride = static_cast<int64_t>(num_kv_heads) * Gm::PAGE;
-  const int j_me = lane >> 4;   // page of this lane's token (QK layout)
-  const int t_me = lane & 15;   // token within that page
+  const int j_me = lane / BS;   // page of this lane's token (QK layout)
+  const int t_me = lane % BS;   // token within that page
   const int vrow = lane / LPR;  // value d-row within a wave load
   const int vtok = X * (lane % LPR);  // first token of this lane's value chunk
 
   uint4 kreg[NKC];
-  uint4 vreg[4][NVI];
+  uint4 vreg[NP][NVI];
 #pragma unroll
   for (int c = 0; c < NKC; ++c) kreg[c] = make_uint4(0, 0, 0, 0);
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < NP; ++j)
 #pragma unroll
     for (int k = 0; k < NVI; ++k) vreg[j][k] = make_uint4(0, 0, 0, 0);
   float m[G], l[G], acc[G][NVI];
@@ -213,12 +218,12 @@ __device__ __forceinline__ void decode_item(
   }
 
   const int ntiles = (part_end - part_start + kTile - 1) / kTile;
-  const int lb_part = part_start / kBS;
+  const int lb_part = part_start / BS;
 
   // Block id of this lane's own page (QK layout) for a tile; -1 past the end.
   auto page_id = [&](int tile, int j) -> int {
-    const int lb = lb_part + tile * 4 + j;
-    return lb * kBS < part_end ? bt_row[lb] : -1;
+    const int lb = lb_part + tile * NP + j;
+    return lb * BS < part_end ? bt_row[lb] : -1;
   };
   // Pages past the end of the partition are not loaded: their registers keep
   // stale contents, which no result uses (their scores are replaced by -inf
@@ -227,12 +232,12 @@ __device__ __forceinline__ void decode_item(
     if (phys >= 0) {
       const T* base = kc + phys * blk_stride + head_off + kofs;
 #pragma unroll
-      for (int c = 0; c < NKC; ++c) kreg[c] = ld16(base + c * (kBS * X));
+      for (int c = 0; c < NKC; ++c) kreg[c] = ld16(base + c * (BS * X));
     }
   };
-  auto load_v = [&](const int (&ids)[4], int vofs) {
+  auto load_v = [&](const int (&ids)[NP], int vofs) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NP; ++j) {
       if (ids[j] >= 0) {
         const T* base = vc + ids[j] * blk_stride + head_off + vofs;
 #pragma unroll
@@ -240,9 +245,9 @@ __device__ __forceinline__ void decode_item(
       }
     }
   };
-  auto page_ids = [&](int my, int (&ids)[4]) {
+  auto page_ids = [&](int my, int (&ids)[NP]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ids[j] = __builtin_amdgcn_readlane(my, 16 * j);
+    for (int j = 0; j < NP; ++j) ids[j] = __builtin_amdgcn_readlane(my, BS * j);
   };
 
   // Software pipeline inside the wave: block ids are fetched two tiles ahead;
@@ -261,7 +266,7 @@ __device__ __forceinline__ void decode_item(
   constexpr bool kPipe = G <= 2;
   int id_cur = page_id(0, j_me);
   int id_next = ntiles > 1 ? page_id(1, j_me) : -1;
-  int ids[4];
+  int ids[NP];
   page_ids(id_cur, ids);
   load_k(id_cur, t_me * X);
   if (kEarlyV) load_v(ids, lane * X);
@@ -314,7 +319,7 @@ __device__ __forceinline__ void decode_item(
         for (int h = 0; h < G; ++h) sc[h] = dot_chunk(sc[h], q_const[h * NKC + c], kreg[c]);
       }
     }
-    int ids_next[4];
+    int ids_next[NP];
     page_ids(id_next, ids_next);
     {
       int vofs = lane * X, kofs = t_me * X;
@@ -348,8 +353,8 @@ __device__ __forceinline__ void decode_item(
     // ---- weighted values
     if (tile_start + kTile > part_end) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int keep = part_end - (tile_start + 16 * j + vtok);
+      for (int j = 0; j < NP; ++j) {
+        const int keep = part_end - (tile_start + BS * j + vtok);
         if (keep < X) {
 #pragma unroll
           for (int k = 0; k < NVI; ++k) vreg[j][k] = mask_chunk<T>(vreg[j][k], keep);
@@ -357,9 +362,9 @@ __device__ __forceinline__ void decode_item(
       }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NP; ++j) {
       if (ids[j] < 0) continue;
-      int pofs = 16 * j + vtok;
+      int pofs = BS * j + vtok;
       if (G > 2) asm volatile("" : "+v"(pofs));  // weights of one page at a time
 #pragma unroll
       for (int h = 0; h < G; ++h) {
@@ -414,7 +419,7 @@ __device__ __forceinline__ void decode_item(
       load_v(ids_next, vofs);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ids[j] = ids_next[j];
+    for (int j = 0; j < NP; ++j) ids[j] = ids_next[j];
     id_cur = id_next;
     id_next = id_next2;
   }
@@ -428,8 +433,11 @@ __device__ __forceinline__ void decode_item(
 #pragma unroll
     for (int k = 0; k < NVI; ++k) {
       float a = acc[h][k];
-      a += pa::dpp<pa::kDppXor1>(a);  // lanes sharing a value row: xor 1 (and 2)
-      if (LPR == 4) a += pa::dpp<pa::kDppXor2>(a);
+      // sum over the LPR lanes sharing a value row
+      if (LPR >= 2) a += pa::dpp<pa::kDppXor1>(a);
+      if (LPR >= 4) a += pa::dpp<pa::kDppXor2>(a);
+      if (LPR >= 8) a += pa::dpp<pa::kDppHalfMirror>(a);
+      if (LPR >= 16) a += pa::dpp<pa::kDppMirror>(a);
       const int d = k * DPI + vrow;
       if (lane % LPR == 0) {
         if (nparts_s == 1) {

@@ -35,7 +35,7 @@ def test_host_argument_checks_reject_before_launch():
     fake = ctypes.c_void_p(16)  # never dereferenced: every call fails validation first
     # unsupported head_dim / block_size / dtype
     assert L.pa_reshape_and_cache(fake, fake, fake, fake, fake, 4, 96, 96, 1, 96, 16, 8, PA_BF16, None) == -5
-    assert L.pa_reshape_and_cache(fake, fake, fake, fake, fake, 4, 128, 128, 1, 128, 8, 8, PA_BF16, None) == -5
+    assert L.pa_reshape_and_cache(fake, fake, fake, fake, fake, 4, 128, 128, 1, 128, 12, 8, PA_BF16, None) == -5
     assert L.pa_reshape_and_cache(fake, fake, fake, fake, fake, 4, 128, 128, 1, 128, 16, 8, 7, None) == -5
     # stride smaller than a token row
     assert L.pa_reshape_and_cache(fake, fake, fake, fake, fake, 4, 64, 128, 1, 128, 16, 8, PA_BF16, None) == -1
@@ -55,7 +55,7 @@ def test_host_argument_checks_reject_before_launch():
     assert dec(H=8, part=64) == -6
     assert dec(H=8, maxL=8 * 16 + 1) == -1
     assert dec(H=8, D=96) == -5
-    assert dec(H=8, BS=32) == -5
+    assert dec(H=8, BS=24) == -5
     assert L.pa_decode_workspace_bytes(2, 8, 128, 100, 0) == 0
     assert L.pa_decode_workspace_bytes(2, 8, 128, 64, 64) == 0
     assert L.pa_decode_workspace_bytes(2, 8, 128, 100, 64) >= 2 * 8 * 2 * 130 * 4
