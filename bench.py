@@ -553,6 +553,8 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
 
 DECODE_SOURCES = ("paged_kv_cache_219_amd/csrc/decode.hip",
                   "paged_kv_cache_219_amd/csrc/decode_core.h",
+                  "paged_kv_cache_219_amd/csrc/decode_mfma.h",
+                  "paged_kv_cache_219_amd/csrc/prefill_core.h",
                   "paged_kv_cache_219_amd/csrc/page_ring.h",
                   "paged_kv_cache_219_amd/csrc/pa_device.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pa_decode.decode_bf16.traffic.txt")
