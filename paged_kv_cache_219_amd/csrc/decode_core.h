@@ -9,19 +9,21 @@
 // bound by memory bandwidth: the design goal is to stream every K/V page once
 // at HBM speed.
 //
-// Work decomposition.  One wave (one 64-thread workgroup) per (partition,
-// kv head, sequence).  A partition is a run of `partition` tokens (a multiple
+// Work decomposition.  One wave per item (partition, kv head, sequence): a
+// 64-thread workgroup in decode_kernel, one wave of a 4-wave workgroup in the
+// mixed-batch kernel.  A partition is a run of `partition` tokens (a multiple
 // of 64); a sequence spanning several partitions is processed by independent
 // waves that each emit (m, l, o) -- running max (log2 units), sum of
 // exponentials and normalised partial output -- and a second kernel merges
 // them with weights l_p * 2^(m_p - max m).  The wave walks its partition in
-// tiles of 64 tokens = 4 pages of 16 tokens, prefetching the next tile's
-// block ids, keys and values while it computes on the current one.
+// tiles of 64 tokens = 64 / BS pages of BS tokens (BS = 8, 16, 32 or 64),
+// prefetching the next tile's block ids, keys and values while it computes on
+// the current one.
 //
 // Within a tile:
-//  * QK, one token per lane: lane 16j+t owns token t of page j and loads that
-//    token's whole key row -- with the x-packed key layout the 16 lanes of a
-//    page read 256 contiguous bytes per load.  The G query heads sharing the
+//  * QK, one token per lane: lane BS j + t owns token t of page j and loads
+//    that token's whole key row -- with the x-packed key layout the BS lanes
+//    of a page read 16 BS contiguous bytes per load.  The G query heads sharing the
 //    kv head are wave-uniform and read with scalar loads into SGPRs, which
 //    feed the dot products directly; bf16 products use v_dot2_f32_bf16 (exact
 //    products, fp32 accumulation), so no cross-lane reduction is needed for
