@@ -100,26 +100,33 @@ def bench_decode(name: str, steps: int, warmup: int, grouped: bool = False):
                                                     max_ctx // spec.block_size * spec.block_size,
                                                     spec.partition)
         ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
-        d_grp = torch.empty((B, 3), dtype=torch.int32, device=dev)
-        d_pre = torch.empty(B, dtype=torch.int32, device=dev)
     else:
         ws = decode_workspace(B, spec.num_heads, spec.head_dim, max_ctx, spec.partition, dev)
     seqs = np.array(sc.batch, np.int64)
     ones = np.ones(B, np.int32)
+    # The step's host-made arrays (slots, tables, lengths, copy-on-write pairs,
+    # prefix groups) share one pinned buffer per ring slot and go to the device
+    # in one copy.
+    fields = [("slots", torch.int64, (B,)), ("tab", torch.int32, (B, mb)),
+              ("len", torch.int32, (B,)), ("cow", torch.int32, (B, 2)),
+              ("grp", torch.int32, (B, 3)), ("pre", torch.int32, (B,))]
+    offs, nbytes = {}, 0
+    for f, dt, shape in fields:
+        offs[f] = nbytes
+        nbytes += (int(np.prod(shape)) * torch.tensor([], dtype=dt).element_size() + 255) // 256 * 256
+
+    def carve(buf):
+        return {f: buf[offs[f]:offs[f] + int(np.prod(shape)) * torch.tensor([], dtype=dt).element_size()]
+                .view(dt).view(*shape) for f, dt, shape in fields}
     R = 3  # ring of pinned host buffers
     pin = []
     for _ in range(R):
-        t_slots = torch.empty(B, dtype=torch.int64, pin_memory=True)
-        t_tab = torch.empty((B, mb), dtype=torch.int32, pin_memory=True)
-        t_len = torch.empty(B, dtype=torch.int32, pin_memory=True)
-        t_cow = torch.empty((B, 2), dtype=torch.int32, pin_memory=True)
-        t_grp = torch.empty((B, 3), dtype=torch.int32, pin_memory=True)
-        t_pre = torch.empty(B, dtype=torch.int32, pin_memory=True)
-        pin.append((t_slots, t_tab, t_len, t_cow, t_grp, t_pre, torch.cuda.Event()))
-    d_slots = torch.empty(B, dtype=torch.int64, device=dev)
-    d_tab = torch.empty((B, mb), dtype=torch.int32, device=dev)
-    d_len = torch.empty(B, dtype=torch.int32, device=dev)
-    d_cow = torch.empty((B, 2), dtype=torch.int32, device=dev)
+        hb = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+        pin.append((hb, carve(hb), torch.cuda.Event()))
+    d_buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    d = carve(d_buf)
+    d_slots, d_tab, d_len, d_cow = d["slots"], d["tab"], d["len"], d["cow"]
+    d_grp, d_pre = d["grp"], d["pre"]
     stream = torch.cuda.current_stream(dev)
     dec_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(steps)]
@@ -136,25 +143,20 @@ def bench_decode(name: str, steps: int, warmup: int, grouped: bool = False):
             torch.cuda.synchronize()
             wall0 = time.perf_counter()
             t0.record(stream)
-        t_slots, t_tab, t_len, t_cow, t_grp, t_pre, ev = pin[i % R]
-        ev.synchronize()  # the copies that last read this ring slot are done
+        hb, h, ev = pin[i % R]
+        ev.synchronize()  # the copy that last read this ring slot is done
         slots, cow, tables, lens = w.alloc.batch_append(
-            seqs, ones, mb, tables_out=t_tab.numpy(), lens_out=t_len.numpy(),
-            slots_out=t_slots.numpy(), cow_out=t_cow.numpy())
-        d_slots.copy_(t_slots, non_blocking=True)
-        d_tab.copy_(t_tab, non_blocking=True)
-        d_len.copy_(t_len, non_blocking=True)
+            seqs, ones, mb, tables_out=h["tab"].numpy(), lens_out=h["len"].numpy(),
+            slots_out=h["slots"].numpy(), cow_out=h["cow"].numpy())
         if grouped:
             groups, pre, max_pre = pa_prefix_plan(tables, lens)
             ng = len(groups)
-            t_grp.numpy()[:ng] = groups
-            t_pre.numpy()[:] = pre
-            if ng:
-                d_grp[:ng].copy_(t_grp[:ng], non_blocking=True)
-            d_pre.copy_(t_pre, non_blocking=True)
+            h["grp"].numpy()[:ng] = groups
+            h["pre"].numpy()[:] = pre
             plan_groups = ng
-        if len(cow):
-            d_cow[: len(cow)].copy_(t_cow[: len(cow)], non_blocking=True)
+        # prefix groups only when grouped, copy-on-write pairs only when present
+        n_copy = nbytes if grouped else (offs["grp"] if len(cow) else offs["cow"])
+        d_buf[:n_copy].copy_(hb[:n_copy], non_blocking=True)
         ev.record(stream)
         if len(cow):
             pa_copy_blocks(w.k_cache, w.v_cache, d_cow[: len(cow)])
