@@ -299,8 +299,8 @@ int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* 
  *   workspace        device scratch of pa_mixed_step_workspace_bytes(...)
  *                    bytes (NULL when that is 0), as in pa_decode.
  * Prefill rows are computed by the pa_prefill_chunk workgroup (bit-identical
- * to it), decode rows by the one-wave decode body (bit-identical to pa_decode
- * with the same partition when num_heads / num_kv_heads is 1 or 2).  bf16,
+ * to it), decode rows by pa_decode's per-item bodies (bit-identical to
+ * pa_decode with the same partition).  bf16,
  * head_dim 128, num_heads / num_kv_heads in {1, 2, 4, 8}.
  */
 int pa_mixed_step(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -223,16 +223,16 @@ __device__ __forceinline__ void mfma_decode_range(
   }
 }
 
-// Grouped-query decode on the matrix cores: one wave per item (partition,
-// sequence, kv head) in decode_kernel's order, its G query heads as columns.
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(
-    uint16_t* __restrict__ out, Partials ws, const uint16_t* __restrict__ q,
+// Grouped-query decode on the matrix cores: item li (partition, sequence, kv
+// head) in decode_kernel's order, its G query heads as columns, run by the
+// calling wave.
+__device__ __forceinline__ void mfma_decode_item(
+    uint32_t li, uint16_t* __restrict__ out, Partials ws, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ block_tables, int32_t max_blocks,
     const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t num_heads,
     int32_t num_kv_heads, int32_t num_parts, int32_t partition, float scale_log2,
     RangeSplit rs) {
-  const uint32_t li = blockIdx.x;
   const int g = static_cast<int>(li % static_cast<uint32_t>(num_kv_heads));
   const uint32_t ps = li / static_cast<uint32_t>(num_kv_heads);
   const int s = static_cast<int>(ps % static_cast<uint32_t>(num_seqs));
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const int64_t row0 = static_cast<int64_t>(s) * num_heads + static_cast<int64_t>(g) * G;
   if (L <= 0) {
     if (part == 0)
-      for (int i = threadIdx.x; i < G * kD; i += 64) out[row0 * kD + i] = 0;
+      for (int i = threadIdx.x & 63; i < G * kD; i += 64) out[row0 * kD + i] = 0;
     return;
   }
   const int begin = rs.starts ? split_begin(rs.starts[s], L) : 0;
@@ -261,6 +261,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
         out_off = whole ? (row0 + i) * kD : -1;
         part_row = whole ? -1 : (row0 + i) * num_parts + rs.part_base + part;
       });
+}
+
+// One wave (one 64-thread workgroup) per item.
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(
+    uint16_t* __restrict__ out, Partials ws, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const int32_t* __restrict__ block_tables, int32_t max_blocks,
+    const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t num_parts, int32_t partition, float scale_log2,
+    RangeSplit rs) {
+  mfma_decode_item(blockIdx.x, out, ws, q, kc, vc, block_tables, max_blocks, context_lens,
+                   num_seqs, num_heads, num_kv_heads, num_parts, partition, scale_log2, rs);
 }
 
 }  // namespace

@@ -9,14 +9,17 @@
 // finished sequences leave it (continuous batching).  One launch serves the whole batch:
 //  * workgroups [0, prefill workgroups) run the chunked-prefill workgroup of
 //    prefill_core.h (matrix cores, 128 query rows of one (sequence, head));
-//  * the rest run four decode items each, one per wave, with the one-wave
-//    decode body of decode_core.h: an item is a (partition, decode sequence,
-//    kv head) as in pa_decode, and decode sequences longer than one partition
-//    are merged afterwards by pa_decode's second pass (the only other launch).
+//  * the rest run four decode items each, one per wave, with pa_decode's
+//    bodies: the one-wave body of decode_core.h for 1 or 2 query heads per kv
+//    head, the matrix-core body of decode_mfma.h for 4 or 8.  An item is a
+//    (partition, decode sequence, kv head) as in pa_decode, and decode
+//    sequences longer than one partition are merged afterwards by pa_decode's
+//    second pass (the only other launch).
 // The long prefill workgroups are dispatched first and the short decode items
 // fill the chip behind them, so neither part waits for the other's tail.
 
 #include "decode_core.h"
+#include "decode_mfma.h"
 #include "prefill_core.h"
 
 namespace {
@@ -34,7 +37,7 @@ __global__ __launch_bounds__(kMixedWaves * 64, 2) void mixed_step_kernel(
     float scale_log2) {
   constexpr bool PVB = G >= 4;
   __shared__ StepBuf buf[kRing];
-  __shared__ __attribute__((aligned(16))) weight_t<PVB> p_lds[kMixedWaves][G * kTile];
+  __shared__ __attribute__((aligned(16))) weight_t<PVB> p_lds[kMixedWaves][G >= 4 ? 1 : G * kTile];
   if (blockIdx.x < prefill_wgs) {
     prefill_tile<kMixedWaves, 1>(blockIdx.x, buf, out, q, kc, vc, block_tables, max_blocks, qsl,
                                  context_lens, num_prefill_seqs, num_heads, num_kv_heads,
@@ -45,11 +48,17 @@ __global__ __launch_bounds__(kMixedWaves * 64, 2) void mixed_step_kernel(
   const uint32_t item = (blockIdx.x - prefill_wgs) * kMixedWaves + wave;
   const int64_t row0 = num_prefill_tokens * num_heads * kD;  // first decode query row
   // items: kv head fastest, then decode sequence, then partition
-  decode_item<uint16_t, kD, G, PVB>(
-      item, p_lds[wave], out + row0, ws, q + row0, kc, vc,
-      block_tables + static_cast<int64_t>(num_prefill_seqs) * max_blocks, max_blocks,
-      context_lens + num_prefill_seqs, num_decode_seqs, num_heads, num_kv_heads, decode_parts,
-      decode_partition, scale_log2, RangeSplit{nullptr, 0, decode_partition});
+  const int32_t* bt = block_tables + static_cast<int64_t>(num_prefill_seqs) * max_blocks;
+  const RangeSplit rs{nullptr, 0, decode_partition};
+  if constexpr (G >= 4)
+    mfma_decode_item(item, out + row0, ws, q + row0, kc, vc, bt, max_blocks,
+                     context_lens + num_prefill_seqs, num_decode_seqs, num_heads, num_kv_heads,
+                     decode_parts, decode_partition, scale_log2, rs);
+  else
+    decode_item<uint16_t, kD, G, PVB>(item, p_lds[wave], out + row0, ws, q + row0, kc, vc, bt,
+                                      max_blocks, context_lens + num_prefill_seqs,
+                                      num_decode_seqs, num_heads, num_kv_heads, decode_parts,
+                                      decode_partition, scale_log2, rs);
 }
 
 // Decode partition used for a requested one (0: one partition covering the
