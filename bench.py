@@ -145,7 +145,7 @@ def bench_decode(name: str, steps: int, warmup: int, grouped: bool = False):
             t0.record(stream)
         hb, h, ev = pin[i % R]
         ev.synchronize()  # the copy that last read this ring slot is done
-        slots, cow, tables, lens = w.alloc.batch_append(
+        _, cow, tables, lens = w.alloc.batch_append(
             seqs, ones, mb, tables_out=h["tab"].numpy(), lens_out=h["len"].numpy(),
             slots_out=h["slots"].numpy(), cow_out=h["cow"].numpy())
         if grouped:
@@ -229,7 +229,7 @@ def bench_prefill(name: str, steps: int, warmup: int):
     dev = torch.device("cuda")
     w = DeviceWorkload(sc, device=dev, poison=False)
     slots = w.run_step()  # allocate and write the chunk once
-    bt, lens, _, lens_h = w.batch_tables()
+    bt, lens, _, _ = w.batch_tables()
     qsl = w.query_start_loc()
     q = w.queries(0)
     out = torch.empty_like(q)
@@ -287,7 +287,6 @@ def bench_prefix_cache(steps: int, warmup: int):
     bs, H, D = 16, 32, 128
     reqs = multi_turn_requests(6, dialogues=16, turns=4, system_len=1024, user_len=64,
                                answer_len=192, vocab=32000)
-    last = [r for r in reqs if r[1] == 3]
     need = sum(-(-(len(p) + len(a)) // bs) for _, _, p, a in reqs)
     nb = need  # room for every history: nothing is evicted
     alloc = BlockAllocator(nb, bs, np.random.default_rng(6).permutation(nb).astype(np.int32))
