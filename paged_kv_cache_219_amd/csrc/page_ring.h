@@ -27,7 +27,7 @@ constexpr int kD = 128;
 constexpr int kPages = 2;
 constexpr int kStep = kPages * kBS;   // tokens per step
 constexpr int kPageElems = kBS * kD;  // elements of one (block, kv head) page
-constexpr int kRing = 4;
+constexpr int kRing = 3;  // 48 KB per workgroup: three workgroups share a CU's 160 KB
 
 struct StepBuf {
   uint4 k[kPages * 256];

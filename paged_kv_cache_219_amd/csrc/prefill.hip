@@ -16,7 +16,7 @@ constexpr int kBlocks = PA_PREFILL_BLOCKS;
 constexpr int kRowsPerWG = kWaves * 32 * kBlocks;
 
 template <int W, int NB>
-__global__ __launch_bounds__(W * 64, NB == 1 ? 2 : 1) void prefill_chunk_kernel(
+__global__ __launch_bounds__(W * 64, NB == 1 ? 3 : 1) void prefill_chunk_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ block_tables, int32_t max_blocks,
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ context_lens, int32_t num_seqs,

@@ -15,8 +15,8 @@
 // Work decomposition.  A workgroup of 4 waves owns 128 consecutive query rows
 // of one (sequence, head); each wave owns 32 of them.  The workgroup walks the
 // keys/values in steps of 32 tokens (two 16-token pages): each step's K and V
-// pages are copied once, cooperatively, into a ring of four LDS step buffers
-// with direct-to-LDS loads issued three steps ahead of use, then every wave
+// pages are copied once, cooperatively, into a ring of three LDS step buffers
+// with direct-to-LDS loads issued two steps ahead of use, then every wave
 // computes, in transposed form so no operand needs a shuffle,
 //   S^T[32 tokens x 32 queries] = K Q^T    (8 MFMAs over head_dim 128)
 //   O^T[128 dims x 32 queries] += V^T P^T  (8 MFMAs)
