@@ -183,7 +183,8 @@ def bench_decode(name: str, steps: int, warmup: int, grouped: bool = False):
     for tables, lens in snap:
         uniq_total += unique_kv_bytes(tables, lens, spec)
     step_ms = t0.elapsed_time(t1) / steps
-    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in dec_ev]))
+    dec_t = np.array([a.elapsed_time(b) for a, b in dec_ev])
+    dec_ms = float(np.mean(dec_t))
     kv_step = kv_total / steps
     res = {
         "workload": name, "entry": "pa_decode_shared_prefix" if grouped else "pa_decode",
@@ -194,6 +195,8 @@ def bench_decode(name: str, steps: int, warmup: int, grouped: bool = False):
         "step_kv_GBs": kv_step / (step_ms * 1e-3) / 1e9,
         "seq_tokens_per_s": B / (step_ms * 1e-3),
         "decode_ms": dec_ms,
+        "decode_ms_median": float(np.median(dec_t)), "decode_ms_min": float(dec_t.min()),
+        "decode_ms_p90": float(np.percentile(dec_t, 90)),
         "decode_kv_GBs": kv_step / (dec_ms * 1e-3) / 1e9,
         "cow_pairs": ncow_total,
     }
@@ -255,13 +258,16 @@ def bench_prefill(name: str, steps: int, warmup: int):
     t1.record(stream)
     torch.cuda.synchronize()
     step_ms = t0.elapsed_time(t1) / steps
-    pf_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    pf_t = np.array([a.elapsed_time(b) for a, b in ev])
+    pf_ms = float(np.mean(pf_t))
     cached = sc.notes["cached"]
     flops = prefill_flops(cached, sc.query_lens, spec)
     res = {
         "workload": name, "seqs": len(sc.batch), "chunk": max_q, "heads": spec.num_heads,
         "head_dim": spec.head_dim, "cached_tokens": cached,
-        "ms_per_step": step_ms, "prefill_ms": pf_ms, "flops_per_call": flops,
+        "ms_per_step": step_ms, "prefill_ms": pf_ms, "prefill_ms_median": float(np.median(pf_t)),
+        "prefill_ms_min": float(pf_t.min()), "prefill_ms_p90": float(np.percentile(pf_t, 90)),
+        "flops_per_call": flops,
         "prefill_TFLOPs": flops / (pf_ms * 1e-3) / 1e12,
         "query_tokens_per_s": sum(sc.query_lens) / (step_ms * 1e-3),
     }
