@@ -254,7 +254,8 @@ def test_prefill_config_scaled():
 
 @pytest.mark.parametrize("cached,chunk,H,KVH", [([0, 16, 33, 100], 70, 4, 4),
                                                 ([5, 0, 250], 129, 8, 2),
-                                                ([0], 1, 2, 2), ([17, 31], 16, 4, 1)])
+                                                ([0], 1, 2, 2), ([17, 31], 16, 4, 1),
+                                                ([300, 0, 777], 600, 2, 2)])
 def test_prefill_ragged_shapes(cached, chunk, H, KVH):
     say(f"prefill ragged cached={cached} chunk={chunk} H={H} KVH={KVH}")
     spec = Spec("pre", "prefill", H, KVH, 128, 16, "bf16")
