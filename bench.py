@@ -43,6 +43,23 @@ def kv_bytes(lens, spec) -> int:
     return int(np.sum(lens, dtype=np.int64)) * spec.num_kv_heads * spec.head_dim * 2 * esz
 
 
+def blocks_read_once(tables, groups=None, pre=None, block_size: int = 16) -> bool:
+    """True when the decode call reads no physical block twice, so it may pass
+    PA_DECODE_STREAM_KV.  ``tables`` are the call's padded block tables (-1
+    past each sequence's last block).  With prefix groups, a group's prefix
+    pages are read once (from its first member's row) and every sequence's own
+    pages from its prefix on."""
+    t = np.asarray(tables)
+    read = t >= 0
+    if groups is not None and len(groups):
+        skip = np.zeros(t.shape[0], dtype=np.int64)   # leading columns not read per row
+        for first, n, _ in groups:
+            skip[first + 1:first + n] = pre[first + 1:first + n] // block_size
+        read &= np.arange(t.shape[1])[None, :] >= skip[:, None]
+    ids = t[read]
+    return ids.size == 0 or int(np.bincount(ids).max()) <= 1
+
+
 def unique_kv_bytes(tables, lens, spec) -> int:
     """KV bytes counting every distinct physical (block, kv head) page's used
     tokens once (shared prefix pages are read once by the method)."""
@@ -137,6 +154,7 @@ def bench_decode(name: str, steps: int, warmup: int, grouped: bool = False):
     ncow_total = 0
     snap = []
     plan_groups = 0
+    streamed = 0
     torch.cuda.synchronize()
     for i in range(total):
         if i == warmup:
@@ -165,12 +183,15 @@ def bench_decode(name: str, steps: int, warmup: int, grouped: bool = False):
         if timed:
             dec_ev[i - warmup][0].record(stream)
         if grouped:
+            once = blocks_read_once(tables, groups, pre, spec.block_size)
             pa_decode_shared_prefix(out, qs[i], w.k_cache, w.v_cache, d_tab, d_len, spec.scale,
                                     spec.partition, int(lens.max()), d_grp[:ng], d_pre, max_pre,
-                                    ws)
+                                    ws, stream_kv=once)
         else:
+            once = blocks_read_once(tables)
             pa_decode(out, qs[i], w.k_cache, w.v_cache, d_tab, d_len, spec.scale, spec.partition,
-                      int(lens.max()), ws)
+                      int(lens.max()), ws, stream_kv=once)
+        streamed += once
         if timed:
             dec_ev[i - warmup][1].record(stream)
             kv_total += kv_bytes(lens, spec)
@@ -199,6 +220,7 @@ def bench_decode(name: str, steps: int, warmup: int, grouped: bool = False):
         "decode_ms_p90": float(np.percentile(dec_t, 90)),
         "decode_kv_GBs": kv_step / (dec_ms * 1e-3) / 1e9,
         "cow_pairs": ncow_total,
+        "stream_kv_calls": int(streamed),
     }
     if grouped:
         res["prefix_groups"] = plan_groups
@@ -397,13 +419,15 @@ def bench_mixed(steps: int, warmup: int):
     ws_m = torch.empty(max(1, lib().pa_mixed_step_workspace_bytes(Dn, H, D, max(dlens), 256)),
                        dtype=torch.uint8, device=dev)
     scale = float(np.float32(1 / np.sqrt(D)))
+    once = blocks_read_once(tables[P:])  # the flag governs the decode items' reads
     runs = {
         "mixed": lambda: pa_mixed_step(out, q, kc, vc, bt, qsl_p, ln, T, chunk, max(dlens), scale,
-                                       256, ws_m),
+                                       256, ws_m, stream_kv=once),
         "mixed_unsplit": lambda: pa_mixed_step(out, q, kc, vc, bt, qsl_p, ln, T, chunk, max(dlens),
-                                               scale, 0),
+                                               scale, 0, stream_kv=once),
         "split": lambda: (pa_prefill_chunk(out, q, kc, vc, bt_p, qsl_p, ln_p, chunk, scale),
-                          pa_decode(out_d, q_d, kc, vc, bt_d, ln_d, scale, 256, max(dlens), ws)),
+                          pa_decode(out_d, q_d, kc, vc, bt_d, ln_d, scale, 256, max(dlens), ws,
+                                    stream_kv=once)),
         "as_prefill": lambda: pa_prefill_chunk(out, q, kc, vc, bt, qsl_all, ln, chunk, scale),
     }
     stream = torch.cuda.current_stream(dev)
@@ -478,7 +502,8 @@ def bench_block_sizes(steps: int, warmup: int):
             for it in range(warmup + steps):
                 if it >= warmup:
                     ev[it - warmup][0].record(stream)
-                pa_decode(out, q, kc, vc, bt, ln, scale, part, max(lens_l), ws)
+                pa_decode(out, q, kc, vc, bt, ln, scale, part, max(lens_l), ws,
+                          stream_kv=blocks_read_once(tables))
                 if it >= warmup:
                     ev[it - warmup][1].record(stream)
             torch.cuda.synchronize()

@@ -22,6 +22,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "pa.h")
 PA_OK = 0
 PA_F32 = 0
 PA_BF16 = 1
+PA_DECODE_STREAM_KV = 1
 STATUS = {0: "PA_OK", -1: "PA_ERR_INVALID_ARG", -2: "PA_ERR_NO_FREE_BLOCKS",
           -3: "PA_ERR_UNKNOWN_SEQ", -4: "PA_ERR_SEQ_EXISTS", -5: "PA_ERR_UNSUPPORTED",
           -6: "PA_ERR_WORKSPACE", -7: "PA_ERR_DEVICE"}
@@ -41,18 +42,18 @@ _SIGS = {
     "pa_copy_blocks": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
     "pa_decode_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32, c_i32,
-                          c_i32, c_i32, c_f32, c_i32, c_i32, c_vp, c_sz, c_i32, c_vp]),
+                          c_i32, c_i32, c_f32, c_i32, c_i32, c_vp, c_sz, c_i32, c_i32, c_vp]),
     "pa_prefix_plan": (c_i32, [c_vp, c_i32, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp,
                                c_vp]),
     "pa_decode_shared_prefix_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_decode_shared_prefix": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32,
                                         c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_i32, c_vp,
-                                        c_i32, c_vp, c_i32, c_vp, c_sz, c_i32, c_vp]),
+                                        c_i32, c_vp, c_i32, c_vp, c_sz, c_i32, c_i32, c_vp]),
     "pa_prefill_chunk": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32,
                                  c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp]),
     "pa_mixed_step": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32,
                               c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp,
-                              c_sz, c_i32, c_vp]),
+                              c_sz, c_i32, c_i32, c_vp]),
     "pa_mixed_step_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_alloc_create": (c_i32, [c_i32, c_i32, c_vp, ctypes.POINTER(c_vp)]),
     "pa_alloc_destroy": (None, [c_vp]),

@@ -520,6 +520,6 @@ const char* pa_status_str(int status) {
   }
 }
 
-int pa_version(void) { return 1; }
+int pa_version(void) { return 2; }
 
 }  // extern "C"

@@ -8,7 +8,7 @@
 namespace {
 
 // One wave (one 64-thread workgroup) per item.
-template <typename T, int D, int G, bool PVB, int BS>
+template <typename T, int D, int G, bool PVB, int BS, bool NT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(
     T* __restrict__ out, Partials ws, const T* __restrict__ q, const T* __restrict__ kc,
     const T* __restrict__ vc, const int32_t* __restrict__ block_tables, int32_t max_blocks,
@@ -16,7 +16,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     int32_t num_kv_heads, int32_t num_parts, int32_t partition, float scale_log2,
     RangeSplit rs) {
   __shared__ __attribute__((aligned(16))) weight_t<PVB> p_lds[G * kTile];
-  decode_item<T, D, G, PVB, BS>(blockIdx.x, p_lds, out, ws, q, kc, vc, block_tables,
+  decode_item<T, D, G, PVB, BS, NT>(blockIdx.x, p_lds, out, ws, q, kc, vc, block_tables,
                                 max_blocks, context_lens, num_seqs, num_heads, num_kv_heads,
                                 num_parts, partition, scale_log2, rs);
 }
@@ -35,6 +35,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 // fits one partition.
 constexpr int kPrefixMembers = PA_PREFIX_MAX_MEMBERS;
 
+template <bool NT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_prefix_mfma_kernel(
     uint16_t* __restrict__ out, Partials ws, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     const int s = first + gq / gq_heads;
     return static_cast<int64_t>(s) * num_heads + g * gq_heads + gq % gq_heads;
   };
-  mfma_decode_range(
+  mfma_decode_range<NT>(
       out, ws, kc, vc, block_tables + static_cast<int64_t>(first) * max_blocks, num_kv_heads, g,
       part_start, min(part_start + partition, P), scale_log2, min(Q, nq - q0),
       [&](int i) { return q + row_of(i) * kD; },
@@ -92,7 +93,7 @@ struct Split {
   RangeSplit rs;
 };
 
-template <typename T, int D, int G, bool PVB, int BS>
+template <typename T, int D, int G, bool PVB, int BS, bool NT>
 int launch_decode(void* out, const void* q, const void* kc, const void* vc, const int32_t* bt,
                   int32_t max_blocks, const int32_t* lens, int32_t B, int32_t H, int32_t KVH,
                   Split sp, int32_t partition, float scale_log2, void* ws, hipStream_t st) {
@@ -102,12 +103,12 @@ int launch_decode(void* out, const void* q, const void* kc, const void* vc, cons
   // 1 or 2 the one-wave body is as fast (both stream at the same rate) and
   // faster where sequences share pages through L2.
   if constexpr (BS == kBS && sizeof(T) == 2 && D == 128 && (G == 4 || G == 8)) {
-    hipLaunchKernelGGL(decode_mfma_kernel, dim3(static_cast<uint32_t>(grid)), dim3(64), 0, st,
+    hipLaunchKernelGGL(decode_mfma_kernel<NT>, dim3(static_cast<uint32_t>(grid)), dim3(64), 0, st,
                        static_cast<uint16_t*>(out), p, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(kc), static_cast<const uint16_t*>(vc), bt,
                        max_blocks, lens, B, H, KVH, sp.slots, partition, scale_log2, sp.rs);
   } else {
-    hipLaunchKernelGGL((decode_kernel<T, D, G, PVB, BS>), dim3(static_cast<uint32_t>(grid)), dim3(64),
+    hipLaunchKernelGGL((decode_kernel<T, D, G, PVB, BS, NT>), dim3(static_cast<uint32_t>(grid)), dim3(64),
                        0, st, static_cast<T*>(out), p, static_cast<const T*>(q),
                        static_cast<const T*>(kc), static_cast<const T*>(vc), bt, max_blocks, lens,
                        B, H, KVH, sp.slots, partition, scale_log2, sp.rs);
@@ -122,15 +123,21 @@ template <typename T, int D, int BS = kBS>
 int dispatch_group(int G, void* out, const void* q, const void* kc, const void* vc,
                    const int32_t* bt, int32_t mb, const int32_t* lens, int32_t B, int32_t H,
                    int32_t KVH, Split sp, int32_t partition, float sl2, void* ws,
-                   hipStream_t st) {
+                   hipStream_t st, bool nt) {
   constexpr bool kBf = sizeof(T) == 2;
+#define PA_LAUNCH(GG, PV)                                                                        \
+  (nt ? launch_decode<T, D, GG, PV, BS, true>(out, q, kc, vc, bt, mb, lens, B, H, KVH, sp,        \
+                                               partition, sl2, ws, st)                           \
+      : launch_decode<T, D, GG, PV, BS, false>(out, q, kc, vc, bt, mb, lens, B, H, KVH, sp,       \
+                                                partition, sl2, ws, st))
   switch (G) {
-    case 1: return launch_decode<T, D, 1, false, BS>(out, q, kc, vc, bt, mb, lens, B, H, KVH, sp, partition, sl2, ws, st);
-    case 2: return launch_decode<T, D, 2, false, BS>(out, q, kc, vc, bt, mb, lens, B, H, KVH, sp, partition, sl2, ws, st);
-    case 4: return launch_decode<T, D, 4, kBf, BS>(out, q, kc, vc, bt, mb, lens, B, H, KVH, sp, partition, sl2, ws, st);
-    case 8: return launch_decode<T, D, 8, kBf, BS>(out, q, kc, vc, bt, mb, lens, B, H, KVH, sp, partition, sl2, ws, st);
+    case 1: return PA_LAUNCH(1, false);
+    case 2: return PA_LAUNCH(2, false);
+    case 4: return PA_LAUNCH(4, kBf);
+    case 8: return PA_LAUNCH(8, kBf);
     default: return PA_ERR_UNSUPPORTED;
   }
+#undef PA_LAUNCH
 }
 
 // dtype and head_dim dispatch for one block size
@@ -138,15 +145,15 @@ template <int BS>
 int dispatch_block(int32_t dtype, int32_t head_dim, int G, void* out, const void* q,
                    const void* kc, const void* vc, const int32_t* bt, int32_t mb,
                    const int32_t* lens, int32_t B, int32_t H, int32_t KVH, Split sp,
-                   int32_t partition, float sl2, void* ws, hipStream_t st) {
+                   int32_t partition, float sl2, void* ws, hipStream_t st, bool nt) {
   if (dtype == PA_BF16) {
     if (head_dim == 128)
-      return dispatch_group<uint16_t, 128, BS>(G, out, q, kc, vc, bt, mb, lens, B, H, KVH, sp, partition, sl2, ws, st);
-    return dispatch_group<uint16_t, 64, BS>(G, out, q, kc, vc, bt, mb, lens, B, H, KVH, sp, partition, sl2, ws, st);
+      return dispatch_group<uint16_t, 128, BS>(G, out, q, kc, vc, bt, mb, lens, B, H, KVH, sp, partition, sl2, ws, st, nt);
+    return dispatch_group<uint16_t, 64, BS>(G, out, q, kc, vc, bt, mb, lens, B, H, KVH, sp, partition, sl2, ws, st, nt);
   }
   if (head_dim == 128)
-    return dispatch_group<float, 128, BS>(G, out, q, kc, vc, bt, mb, lens, B, H, KVH, sp, partition, sl2, ws, st);
-  return dispatch_group<float, 64, BS>(G, out, q, kc, vc, bt, mb, lens, B, H, KVH, sp, partition, sl2, ws, st);
+    return dispatch_group<float, 128, BS>(G, out, q, kc, vc, bt, mb, lens, B, H, KVH, sp, partition, sl2, ws, st, nt);
+  return dispatch_group<float, 64, BS>(G, out, q, kc, vc, bt, mb, lens, B, H, KVH, sp, partition, sl2, ws, st, nt);
 }
 
 
@@ -164,8 +171,9 @@ extern "C" int pa_decode(void* out, const void* q, const void* k_cache, const vo
                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                          int32_t num_blocks, float scale, int32_t partition,
                          int32_t max_context_len, void* workspace, size_t workspace_bytes,
-                         int32_t dtype, void* stream) {
+                         int32_t dtype, int32_t flags, void* stream) {
   if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (flags & ~PA_DECODE_STREAM_KV) return PA_ERR_INVALID_ARG;
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
       num_blocks <= 0 || partition < 0 || max_context_len < 0)
     return PA_ERR_INVALID_ARG;
@@ -199,7 +207,7 @@ extern "C" int pa_decode(void* out, const void* q, const void* k_cache, const vo
 #define PA_DECODE_BS(BSZ)                                                                      \
   dispatch_block<BSZ>(dtype, head_dim, G, out, q, k_cache, v_cache, block_tables,              \
                       max_blocks_per_seq, context_lens, num_seqs, num_heads, num_kv_heads, sp, \
-                      part, sl2, workspace, st)
+                      part, sl2, workspace, st, (flags & PA_DECODE_STREAM_KV) != 0)
   switch (block_size) {
     case 8: return PA_DECODE_BS(8);
     case 32: return PA_DECODE_BS(32);
@@ -257,8 +265,10 @@ extern "C" int pa_decode_shared_prefix(
     int32_t block_size, int32_t num_blocks, float scale, int32_t partition,
     int32_t max_context_len, const int32_t* prefix_groups, int32_t num_groups,
     const int32_t* seq_prefix_lens, int32_t max_prefix_len, void* workspace,
-    size_t workspace_bytes, int32_t dtype, void* stream) {
+    size_t workspace_bytes, int32_t dtype, int32_t flags, void* stream) {
   if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (flags & ~PA_DECODE_STREAM_KV) return PA_ERR_INVALID_ARG;
+  const bool nt = (flags & PA_DECODE_STREAM_KV) != 0;
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
       num_blocks <= 0 || partition < 0 || max_context_len < 0 || num_groups < 0 ||
       max_prefix_len < 0)
@@ -294,7 +304,8 @@ extern "C" int pa_decode_shared_prefix(
   if (split) {
     const Partials p = carve(workspace, num_seqs, num_heads, 128, slots);
     const int64_t grid = pre * num_groups * nchunks * num_kv_heads;
-    hipLaunchKernelGGL(decode_prefix_mfma_kernel, dim3(static_cast<uint32_t>(grid)), dim3(64), 0,
+    auto kernel = nt ? decode_prefix_mfma_kernel<true> : decode_prefix_mfma_kernel<false>;
+    hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(grid)), dim3(64), 0,
                        st, static_cast<uint16_t*>(out), p, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k_cache),
                        static_cast<const uint16_t*>(v_cache), block_tables, max_blocks_per_seq,
@@ -309,5 +320,5 @@ extern "C" int pa_decode_shared_prefix(
                   prefix_partition(part)}};
   return dispatch_group<uint16_t, 128>(G, out, q, k_cache, v_cache, block_tables,
                                        max_blocks_per_seq, context_lens, num_seqs, num_heads,
-                                       num_kv_heads, sp, part, sl2, workspace, st);
+                                       num_kv_heads, sp, part, sl2, workspace, st, nt);
 }

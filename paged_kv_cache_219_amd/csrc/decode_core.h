@@ -136,7 +136,7 @@ using weight_t = typename std::conditional<PVB, uint16_t, float>::type;
 
 // One item (partition, sequence, kv head) of the one-wave decode, run by one
 // wave of the calling workgroup; p_lds is that wave's own G * 64 weights.
-template <typename T, int D, int G, bool PVB, int BS = kBS>
+template <typename T, int D, int G, bool PVB, int BS = kBS, bool NT = false>
 __device__ __forceinline__ void decode_item(
     uint32_t li, weight_t<PVB>* __restrict__ p_lds, T* __restrict__ out, Partials ws,
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
@@ -234,7 +234,7 @@ __device__ __forceinline__ void decode_item(
     if (phys >= 0) {
       const T* base = kc + phys * blk_stride + head_off + kofs;
 #pragma unroll
-      for (int c = 0; c < NKC; ++c) kreg[c] = ld16(base + c * (BS * X));
+      for (int c = 0; c < NKC; ++c) kreg[c] = pa::ld16_kv<NT>(base + c * (BS * X));
     }
   };
   auto load_v = [&](const int (&ids)[NP], int vofs) {
@@ -243,7 +243,7 @@ __device__ __forceinline__ void decode_item(
       if (ids[j] >= 0) {
         const T* base = vc + ids[j] * blk_stride + head_off + vofs;
 #pragma unroll
-        for (int k = 0; k < NVI; ++k) vreg[j][k] = ld16(base + k * 64 * X);
+        for (int k = 0; k < NVI; ++k) vreg[j][k] = pa::ld16_kv<NT>(base + k * 64 * X);
       }
     }
   };

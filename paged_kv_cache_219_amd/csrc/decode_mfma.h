@@ -37,7 +37,7 @@ namespace {
 // (128 bf16); dest_of(i, out_off, part_row) says where its result goes: the
 // output row at element offset out_off (>= 0), or partial row part_row (>= 0)
 // of the workspace.  part_start is a multiple of 16.
-template <typename QRow, typename Dest>
+template <bool NT, typename QRow, typename Dest>
 __device__ __forceinline__ void mfma_decode_range(
     uint16_t* __restrict__ out, Partials ws, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ bt_row, int32_t num_kv_heads,
@@ -92,7 +92,7 @@ __device__ __forceinline__ void mfma_decode_range(
       const uint16_t* base = kc + phys * blk_stride + head_off + ofs;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk)  // chunk 2 kk + hh
-        kreg[kk] = *reinterpret_cast<const uint4*>(base + kk * 2 * kBS * 8);
+        kreg[kk] = pa::ld16_kv<NT>(base + kk * 2 * kBS * 8);
     }
   };
   auto load_v = [&](int step, int ofs) {
@@ -102,7 +102,7 @@ __device__ __forceinline__ void mfma_decode_range(
         const uint16_t* base = vc + page(2 * step + pg) * blk_stride + head_off + ofs;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)  // value row dt * 32 + m_row, tokens 8 hh ..
-          vreg[pg][dt] = *reinterpret_cast<const uint4*>(base + dt * 32 * kBS);
+          vreg[pg][dt] = pa::ld16_kv<NT>(base + dt * 32 * kBS);
       }
     }
   };
@@ -226,6 +226,7 @@ __device__ __forceinline__ void mfma_decode_range(
 // Grouped-query decode on the matrix cores: item li (partition, sequence, kv
 // head) in decode_kernel's order, its G query heads as columns, run by the
 // calling wave.
+template <bool NT>
 __device__ __forceinline__ void mfma_decode_item(
     uint32_t li, uint16_t* __restrict__ out, Partials ws, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
@@ -253,7 +254,7 @@ __device__ __forceinline__ void mfma_decode_item(
                                  : (L + partition - 1) / partition;
   if (nparts_s > 1 && ws.o == nullptr) return;
   const bool whole = nparts_s == 1;
-  mfma_decode_range(
+  mfma_decode_range<NT>(
       out, ws, kc, vc, block_tables + static_cast<int64_t>(s) * max_blocks, num_kv_heads, g,
       part_start, min(part_start + partition, L), scale_log2, G,
       [&](int i) { return q + (row0 + i) * kD; },
@@ -264,6 +265,7 @@ __device__ __forceinline__ void mfma_decode_item(
 }
 
 // One wave (one 64-thread workgroup) per item.
+template <bool NT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(
     uint16_t* __restrict__ out, Partials ws, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
@@ -271,7 +273,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t num_heads,
     int32_t num_kv_heads, int32_t num_parts, int32_t partition, float scale_log2,
     RangeSplit rs) {
-  mfma_decode_item(blockIdx.x, out, ws, q, kc, vc, block_tables, max_blocks, context_lens,
+  mfma_decode_item<NT>(blockIdx.x, out, ws, q, kc, vc, block_tables, max_blocks, context_lens,
                    num_seqs, num_heads, num_kv_heads, num_parts, partition, scale_log2, rs);
 }
 

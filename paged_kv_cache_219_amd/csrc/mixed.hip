@@ -26,7 +26,7 @@ namespace {
 
 constexpr int kMixedWaves = 4;
 
-template <int G>
+template <int G, bool NT>
 __global__ __launch_bounds__(kMixedWaves * 64, 2) void mixed_step_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ block_tables, int32_t max_blocks,
@@ -51,11 +51,11 @@ __global__ __launch_bounds__(kMixedWaves * 64, 2) void mixed_step_kernel(
   const int32_t* bt = block_tables + static_cast<int64_t>(num_prefill_seqs) * max_blocks;
   const RangeSplit rs{nullptr, 0, decode_partition};
   if constexpr (G >= 4)
-    mfma_decode_item(item, out + row0, ws, q + row0, kc, vc, bt, max_blocks,
+    mfma_decode_item<NT>(item, out + row0, ws, q + row0, kc, vc, bt, max_blocks,
                      context_lens + num_prefill_seqs, num_decode_seqs, num_heads, num_kv_heads,
                      decode_parts, decode_partition, scale_log2, rs);
   else
-    decode_item<uint16_t, kD, G, PVB>(item, p_lds[wave], out + row0, ws, q + row0, kc, vc, bt,
+    decode_item<uint16_t, kD, G, PVB, kBS, NT>(item, p_lds[wave], out + row0, ws, q + row0, kc, vc, bt,
                                       max_blocks, context_lens + num_prefill_seqs,
                                       num_decode_seqs, num_heads, num_kv_heads, decode_parts,
                                       decode_partition, scale_log2, rs);
@@ -86,15 +86,18 @@ extern "C" int pa_mixed_step(void* out, const void* q, const void* k_cache, cons
                              int32_t max_decode_context, int32_t num_heads, int32_t num_kv_heads,
                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
                              float scale, int32_t partition, void* workspace,
-                             size_t workspace_bytes, int32_t dtype, void* stream) {
+                             size_t workspace_bytes, int32_t dtype, int32_t flags,
+                             void* stream) {
   if (dtype != PA_BF16 && dtype != PA_F32) return PA_ERR_UNSUPPORTED;
   if (num_prefill_seqs < 0 || num_prefill_tokens < 0 || max_query_len < 0 ||
       num_decode_seqs < 0 || max_decode_context < 0 || num_heads <= 0 || num_kv_heads <= 0 ||
       max_blocks_per_seq <= 0 || num_blocks <= 0 || partition < 0 || partition % kTile != 0)
     return PA_ERR_INVALID_ARG;
   if (num_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (flags & ~PA_DECODE_STREAM_KV) return PA_ERR_INVALID_ARG;
   if (dtype != PA_BF16 || head_dim != kD || block_size != kBS) return PA_ERR_UNSUPPORTED;
   const int G = num_heads / num_kv_heads;
+  const bool nt = (flags & PA_DECODE_STREAM_KV) != 0;
   if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(max_decode_context) > static_cast<int64_t>(max_blocks_per_seq) * kBS)
     return PA_ERR_INVALID_ARG;
@@ -123,7 +126,8 @@ extern "C" int pa_mixed_step(void* out, const void* q, const void* k_cache, cons
   const dim3 grid(static_cast<uint32_t>(pf_wgs + dec_wgs)), block(kMixedWaves * 64);
   hipStream_t st = static_cast<hipStream_t>(stream);
 #define PA_MIXED_LAUNCH(GG)                                                                      \
-  hipLaunchKernelGGL((mixed_step_kernel<GG>), grid, block, 0, st, static_cast<uint16_t*>(out),  \
+  hipLaunchKernelGGL((nt ? mixed_step_kernel<GG, true> : mixed_step_kernel<GG, false>), grid,   \
+                     block, 0, st, static_cast<uint16_t*>(out),                                  \
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),    \
                      static_cast<const uint16_t*>(v_cache), block_tables, max_blocks_per_seq,   \
                      query_start_loc, context_lens, num_prefill_seqs,                            \

@@ -13,7 +13,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from ._lib import PA_BF16, PA_F32, check, lib
+from ._lib import PA_BF16, PA_DECODE_STREAM_KV, PA_F32, check, lib
 
 BLOCK_SIZE = 16
 _DT = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
@@ -37,6 +37,10 @@ def new_kv_cache(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: torch
 
 def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _flags(stream_kv: bool) -> int:
+    return PA_DECODE_STREAM_KV if stream_kv else 0
 
 
 def _dtype(t: torch.Tensor) -> int:
@@ -113,7 +117,10 @@ def decode_workspace(num_seqs, num_heads, head_dim, max_context_len, partition, 
 
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float, partition: int,
-              max_context_len: int, workspace=None, check_device_args=False):
+              max_context_len: int, workspace=None, check_device_args=False,
+              stream_kv: bool = False):
+    """``stream_kv``: PA_DECODE_STREAM_KV, for calls in which no block is read
+    by two sequences (see include/pa.h)."""
     nb, kvh, d, bs = _cache_dims(k_cache, v_cache)
     B, H = q.shape[0], q.shape[1]
     if q.shape != (B, H, d) or out.shape != q.shape or not (q.is_contiguous() and out.is_contiguous()):
@@ -138,7 +145,7 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float
         out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
         block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(), B, H, kvh, d, bs,
         nb, float(scale), int(partition), int(max_context_len), wptr, wbytes, _dtype(q),
-        _stream(q)))
+        _flags(stream_kv), _stream(q)))
 
 
 def pa_prefix_plan(block_tables, context_lens, max_members: int = 8, min_prefix: int = 256,
@@ -173,7 +180,7 @@ def pa_decode_shared_prefix_workspace_bytes(num_seqs, num_heads, head_dim, max_c
 def pa_decode_shared_prefix(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
                             partition: int, max_context_len: int, prefix_groups,
                             seq_prefix_lens, max_prefix_len: int, workspace=None,
-                            check_device_args=False):
+                            check_device_args=False, stream_kv: bool = False):
     """pa_decode with prefix groups (device int32 tensors [G, 3] and [B], as
     pa_prefix_plan returns them)."""
     nb, kvh, d, bs = _cache_dims(k_cache, v_cache)
@@ -210,7 +217,8 @@ def pa_decode_shared_prefix(out, q, k_cache, v_cache, block_tables, context_lens
         block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(), B, H, kvh, d, bs,
         nb, float(scale), int(partition), int(max_context_len),
         prefix_groups.data_ptr() if ng else None, ng,
-        seq_prefix_lens.data_ptr(), int(max_prefix_len), wptr, wbytes, _dtype(q), _stream(q)))
+        seq_prefix_lens.data_ptr(), int(max_prefix_len), wptr, wbytes, _dtype(q),
+        _flags(stream_kv), _stream(q)))
 
 
 def _check_groups(bt, lens, groups, pre, max_prefix_len, bs):
@@ -259,7 +267,8 @@ def pa_prefill_chunk(out, q, k_cache, v_cache, block_tables, query_start_loc, co
 
 def pa_mixed_step(out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens,
                   num_prefill_tokens: int, max_query_len: int, max_decode_context: int,
-                  scale: float, partition: int = 0, workspace=None, check_device_args=False):
+                  scale: float, partition: int = 0, workspace=None, check_device_args=False,
+                  stream_kv: bool = False):
     """Prefill chunks (the first len(query_start_loc) - 1 sequences) and decode
     tokens (the rest, one query row each, after the chunks' rows) in one
     launch (plus the decode merge when partitioned)."""
@@ -299,4 +308,4 @@ def pa_mixed_step(out, q, k_cache, v_cache, block_tables, query_start_loc, conte
         block_tables.data_ptr(), block_tables.shape[1],
         query_start_loc.data_ptr() if P else None, context_lens.data_ptr(), P,
         int(num_prefill_tokens), int(max_query_len), Dn, int(max_decode_context), H, kvh, d, bs,
-        nb, float(scale), int(partition), wptr, wbytes, _dtype(q), _stream(q)))
+        nb, float(scale), int(partition), wptr, wbytes, _dtype(q), _flags(stream_kv), _stream(q)))

@@ -46,3 +46,14 @@ def test_traffic_summary_scales_by_the_copy_calibration(tmp_path):
     line = [l for l in text.splitlines() if l.startswith("@traffic_bytes_per_call")][0]
     # fetch counts half the bytes (factor 2), writes count them all (factor 1)
     assert float(line.split(":")[1]) == (1000 + 10) * 1024 * 2 + (4 + 2) * 1024
+
+
+def test_blocks_read_once_sees_shared_and_grouped_pages():
+    import numpy as np
+    t = np.array([[1, 2, 3, -1], [1, 2, 6, -1], [7, -1, -1, -1]])
+    assert bench.blocks_read_once(t[[0, 2]])
+    assert not bench.blocks_read_once(t)                  # blocks 1 and 2 read twice
+    g = np.array([[0, 2, 32]])
+    assert bench.blocks_read_once(t, g, np.array([32, 32, 0]), 16)    # grouped: prefix read once
+    g = np.array([[0, 2, 16]])
+    assert not bench.blocks_read_once(t, g, np.array([16, 16, 0]), 16)  # block 2 outside prefix

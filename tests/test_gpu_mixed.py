@@ -64,12 +64,18 @@ def test_mixed_batch_matches_oracle_and_the_separate_launches(H, KVH, partition)
     out_pf = torch.empty_like(q)
     pa_prefill_chunk(out_pf, q, w.k_cache, w.v_cache, bt, qsl_all, lens, chunk, sc.spec.scale)
     # decode rows: the one-wave decode body, bit for bit where pa_decode uses it
+    # (with the non-temporal K/V reads: the cache hint changes no result)
     out_dec = torch.empty_like(q[T:])
     pa_decode(out_dec, q[T:].contiguous(), w.k_cache, w.v_cache, bt[P:].contiguous(),
-              lens[P:].contiguous(), sc.spec.scale, partition, max(DECODE_LENS))
+              lens[P:].contiguous(), sc.spec.scale, partition, max(DECODE_LENS), stream_kv=True)
+    out_nt = torch.empty_like(q)
+    pa_mixed_step(out_nt, q, w.k_cache, w.v_cache, bt, torch.tensor(
+        np.concatenate([[0], np.cumsum([chunk] * P)]).astype(np.int32), device="cuda"), lens,
+        P * chunk, chunk, max(DECODE_LENS), sc.spec.scale, partition=partition, stream_kv=True)
     torch.cuda.synchronize()
     assert np.array_equal(to_host_bits(out[:T]), to_host_bits(out_pf[:T]))
     assert np.array_equal(to_host_bits(out[T:]), to_host_bits(out_dec))
+    assert np.array_equal(to_host_bits(out), to_host_bits(out_nt))
 
 
 @pytest.mark.parametrize("kind", ["decode_only", "prefill_only"])

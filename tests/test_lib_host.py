@@ -25,7 +25,7 @@ def test_library_exports_every_declared_function():
     L = lib()
     missing = [n for n in names if not hasattr(L, n)]
     assert not missing, missing
-    assert L.pa_version() == 1
+    assert L.pa_version() == 2
     for code in range(-7, 1):
         assert L.pa_status_str(code).decode().startswith("PA_")
 
@@ -49,8 +49,9 @@ def test_host_argument_checks_reject_before_launch():
         a = dict(args, **kw)
         return L.pa_decode(fake, fake, fake, fake, fake, a["mb"], fake, a["B"], a["H"], a["KVH"],
                            a["D"], a["BS"], a["NB"], 0.1, a["part"], a["maxL"], None, 0,
-                           a.get("dt", PA_BF16), None)
+                           a.get("dt", PA_BF16), a.get("flags", 0), None)
     assert dec() == -1
+    assert dec(H=8, flags=2) == -1          # reserved flag bit
     assert dec(H=8, part=100) == -1
     assert dec(H=8, part=64) == -6
     assert dec(H=8, maxL=8 * 16 + 1) == -1

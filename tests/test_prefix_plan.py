@@ -144,8 +144,9 @@ def test_shared_prefix_decode_rejects_before_launch():
         return L.pa_decode_shared_prefix(fake, fake, fake, fake, fake, a["mb"], fake, a["B"], a["H"],
                                          a["KVH"], a["D"], a["BS"], a["NB"], 0.1, a["part"],
                                          a["maxL"], fake, a["ng"], fake, a["maxP"], None, 0,
-                                         a["dt"], None)
+                                         a["dt"], a.get("flags", 0), None)
     assert dec() == -6                      # needs a workspace
+    assert dec(flags=4) == -1               # reserved flag bit
     assert dec(dt=PA_F32) == -5             # bf16 only
     assert dec(D=64) == -5                  # head_dim 128 only
     assert dec(H=24) == -5                  # query groups of 3 heads
