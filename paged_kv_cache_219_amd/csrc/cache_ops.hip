@@ -15,14 +15,16 @@
 
 namespace {
 
-// One wave per (group of X consecutive tokens, kv head), X = 16 / element
-// size: the number of tokens in one 16-byte unit of the d-major value page.
+// One 256-thread workgroup per (group of X consecutive tokens, kv head),
+// X = 16 / element size: the number of tokens in one 16-byte unit of the
+// d-major value page.  Waves 0-1 write the keys, waves 2-3 the values, so the
+// two halves' loads and stores are in flight together.
 //  * keys: the X tokens' rows as 16-byte chunks, each to its x-packed place;
 //  * values: when the group's slots are X consecutive slots starting at a
 //    multiple of X (the common case when a chunk of a sequence is written),
-//    each lane gathers one dimension of the X tokens and stores it as one
-//    16-byte unit of the page; otherwise each token's values are stored
-//    element by element.
+//    each thread gathers one dimension of the X tokens and stores it as one
+//    16-byte unit of the page; otherwise (scattered tokens, e.g. one new
+//    token per sequence) each thread stores its dimension of every token.
 template <int ESIZE>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const uint8_t* __restrict__ key, const uint8_t* __restrict__ value, uint8_t* __restrict__ kc,
@@ -32,33 +34,36 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   typedef typename std::conditional<ESIZE == 2, uint16_t, uint32_t>::type elem_t;
   constexpr int X = 16 / ESIZE;
   const int lane = threadIdx.x & 63;
-  const int64_t w = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  const int64_t grp = w / kvh;
-  const int head = static_cast<int>(w % kvh);
+  const int64_t grp = blockIdx.x / kvh;
+  const int head = static_cast<int>(blockIdx.x % kvh);
   const int64_t tok0 = grp * X;
   if (tok0 >= num_tokens) return;
   const int ntok = static_cast<int>(min(static_cast<int64_t>(X), num_tokens - tok0));
   const int nchunk = head_dim * ESIZE / 16;
 
-  // this group's slots, one per lane (lanes >= ntok hold -1)
+  // this group's slots, one per lane (lanes >= ntok hold -1), in every wave
   const int64_t my_slot = lane < ntok ? slots[tok0 + lane] : -1;
 
-  // ---- keys
-  for (int u = lane; u < X * nchunk; u += 64) {
-    const int j = u / nchunk, c = u - (u / nchunk) * nchunk;
-    const int64_t slot = __shfl(my_slot, j, 64);
-    if (j < ntok && slot >= 0) {
-      const int64_t blk = slot / block_size;
-      const int off = static_cast<int>(slot % block_size);
-      const uint4 v = *reinterpret_cast<const uint4*>(key + (tok0 + j) * kstride_bytes +
-                                                     static_cast<int64_t>(head) * head_dim * ESIZE +
-                                                     c * 16);
-      *reinterpret_cast<uint4*>(
-          kc + ((((blk * kvh + head) * nchunk + c) * block_size) + off) * 16) = v;
+  if (threadIdx.x < 128) {
+    // ---- keys (X * nchunk <= 128 units)
+    for (int u = threadIdx.x; u < X * nchunk; u += 128) {
+      const int j = u / nchunk, c = u - (u / nchunk) * nchunk;
+      const int64_t slot = __shfl(my_slot, j, 64);
+      if (j < ntok && slot >= 0) {
+        const int64_t blk = slot / block_size;
+        const int off = static_cast<int>(slot % block_size);
+        const uint4 v = *reinterpret_cast<const uint4*>(
+            key + (tok0 + j) * kstride_bytes + static_cast<int64_t>(head) * head_dim * ESIZE +
+            c * 16);
+        *reinterpret_cast<uint4*>(
+            kc + ((((blk * kvh + head) * nchunk + c) * block_size) + off) * 16) = v;
+      }
     }
+    return;
   }
 
   // ---- values
+  const int vt = threadIdx.x - 128;
   const int64_t s0 = __shfl(my_slot, 0, 64);
   const bool run = ntok == X && s0 >= 0 && s0 % X == 0 &&
                    __all(lane >= X || my_slot == s0 + lane);
@@ -66,7 +71,7 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const int64_t blk = s0 / block_size;
     const int off = static_cast<int>(s0 % block_size);
     elem_t* vpage = reinterpret_cast<elem_t*>(vc) + (blk * kvh + head) * head_dim * block_size + off;
-    for (int d = lane; d < head_dim; d += 64) {
+    for (int d = vt; d < head_dim; d += 128) {
       elem_t e[X];
 #pragma unroll
       for (int j = 0; j < X; ++j)
@@ -76,15 +81,23 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
           __builtin_bit_cast(uint4, e);
     }
   } else {
-    for (int j = 0; j < ntok; ++j) {
-      const int64_t slot = __shfl(my_slot, j, 64);
-      if (slot < 0) continue;
-      const int64_t blk = slot / block_size;
-      const int off = static_cast<int>(slot % block_size);
-      const elem_t* vsrc = reinterpret_cast<const elem_t*>(value + (tok0 + j) * vstride_bytes) +
-                           static_cast<int64_t>(head) * head_dim;
-      elem_t* vdst = reinterpret_cast<elem_t*>(vc) + (blk * kvh + head) * head_dim * block_size + off;
-      for (int d = lane; d < head_dim; d += 64) vdst[static_cast<int64_t>(d) * block_size] = vsrc[d];
+    for (int d = vt; d < head_dim; d += 128) {
+      elem_t e[X];
+#pragma unroll
+      for (int j = 0; j < X; ++j)
+        if (j < ntok)
+          e[j] = reinterpret_cast<const elem_t*>(value + (tok0 + j) * vstride_bytes)
+              [static_cast<int64_t>(head) * head_dim + d];
+#pragma unroll
+      for (int j = 0; j < X; ++j) {
+        const int64_t slot = __shfl(my_slot, j, 64);
+        if (j < ntok && slot >= 0) {
+          const int64_t blk = slot / block_size;
+          const int off = static_cast<int>(slot % block_size);
+          reinterpret_cast<elem_t*>(vc)[(blk * kvh + head) * head_dim * block_size +
+                                        static_cast<int64_t>(d) * block_size + off] = e[j];
+        }
+      }
     }
   }
 }
@@ -128,8 +141,7 @@ extern "C" int pa_reshape_and_cache(const void* key, const void* value, void* k_
     return PA_ERR_INVALID_ARG;
   if (((key_stride * es) & 15) != 0) return PA_ERR_INVALID_ARG;
   const int64_t groups = (static_cast<int64_t>(num_tokens) + 16 / es - 1) / (16 / es);
-  const int64_t waves = groups * num_kv_heads;
-  const int64_t blocks = (waves + 3) / 4;
+  const int64_t blocks = groups * num_kv_heads;
   if (blocks > 0x7fffffff) return PA_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (es == 2)
