@@ -39,7 +39,7 @@ __global__ __launch_bounds__(kMixedWaves * 64, 2) void mixed_step_kernel(
   __shared__ StepBuf buf[kRing];
   __shared__ __attribute__((aligned(16))) weight_t<PVB> p_lds[kMixedWaves][G >= 4 ? 1 : G * kTile];
   if (blockIdx.x < prefill_wgs) {
-    prefill_tile<kMixedWaves, 1>(blockIdx.x, buf, out, q, kc, vc, block_tables, max_blocks, qsl,
+    prefill_tile<kMixedWaves>(blockIdx.x, buf, out, q, kc, vc, block_tables, max_blocks, qsl,
                                  context_lens, num_prefill_seqs, num_heads, num_kv_heads,
                                  num_qtiles, scale_log2);
     return;

@@ -1,5 +1,6 @@
 // Chunked prefill over a paged KV cache on gfx950 matrix cores: the body of
-// one workgroup, shared by the prefill and mixed-batch kernels.
+// one 128-row workgroup, shared by the prefill and mixed-batch kernels, and
+// the helpers the 256-row ping-pong body (prefill_pingpong.h) also uses.
 //
 // Page "vLLM PagedAttention chuyên sâu: Phân mảnh bộ nhớ KV Cache, Prefill
 // theo khối & Prefix Caching" (locionic.com), sections "Chunked Prefill" and
@@ -12,7 +13,7 @@
 // Causal alignment: query i of the chunk sits at position L - n_q + i and
 // attends to positions 0 .. L - n_q + i.
 //
-// Work decomposition.  A workgroup of 4 waves owns 128 consecutive query rows
+// Work decomposition.  A workgroup of W waves owns 32 W consecutive query rows
 // of one (sequence, head); each wave owns 32 of them.  The workgroup walks the
 // keys/values in steps of 32 tokens (two 16-token pages): each step's K and V
 // pages are copied once, cooperatively, into a ring of three LDS step buffers
@@ -24,9 +25,16 @@
 // 8*(j/4) + 4*(l/32) + j%4 for j = 0..15), each lane owns one query column:
 // the online softmax of a query lives in lanes q and q+32, and the bf16 P^T
 // operand is built in registers from the lane's own scores.  V^T's operand
-// uses the same token order.  O is rescaled only when a query's running max
-// grows by more than 2^8 (the exponentials then stay below 2^8, far inside
-// fp32 and bf16 range; the final O / l is unchanged).
+// uses the same token order.  O is rescaled only when a query's weight would
+// exceed 2^8 against its reference (the exponentials then stay below 2^8, far
+// inside fp32 and bf16 range; the final O / l is unchanged).
+//
+// The vector instructions per step are kept few, since a wave issues about
+// one instruction every four to six cycles: copy and LDS addresses are
+// per-lane constants plus a scalar per step, the block ids a wave copies are
+// preloaded into its lanes, the row sums come from v_dot2 on the bf16
+// weights (the values the products use), and the need to move a reference is
+// read from those sums instead of from a row maximum.
 //
 // Workgroups are mapped so the q-tiles of one (sequence, head) run on the same
 // XCD at the same time: its K/V pages come from HBM once and are served to the
@@ -48,6 +56,10 @@ using pa::ring::StepBuf;
 using pa::ring::vhalf;
 constexpr uint32_t kXcds = 8;
 constexpr float kLazyRescale = 8.f;   // log2 units
+constexpr float kMaxLaneSum = 256.f;  // 2^kLazyRescale
+constexpr uint32_t kStepBytes = sizeof(StepBuf);  // 16 KB
+constexpr uint32_t kVBytes = kStepBytes / 2;      // values follow the keys
+constexpr uint32_t kOnesBf16x2 = 0x3f803f80u;     // two bf16 1.0
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
@@ -58,19 +70,135 @@ __device__ __forceinline__ pa::f32x16_t mfma32(uint4 a, uint4 b, pa::f32x16_t c)
 
 __device__ __forceinline__ float swap32_max(float v) { return fmaxf(v, __shfl_xor(v, 32, 64)); }
 
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
+}
+
+// Maximum of a lane's 16 scores.
+__device__ __forceinline__ float max16(const float (&x)[16]) {
+  return max3(max3(max3(x[0], x[1], x[2]), max3(x[3], x[4], x[5]), max3(x[6], x[7], x[8])),
+              max3(x[9], x[10], x[11]), max3(max3(x[12], x[13], x[14]), x[15], x[15]));
+}
+
+// Zero the bf16 elements of a 16-byte value chunk whose token index (0..7
+// within the chunk) is >= keep.
+__device__ __forceinline__ uint4 keep_tokens(uint4 v, int keep) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] &= (2 * i < keep ? 0x0000ffffu : 0u) | (2 * i + 1 < keep ? 0xffff0000u : 0u);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// 16-byte direct-to-LDS load from the scalar base `sbase` plus the lane's
+// 32-bit byte offset; lane i's bytes land at LDS address lds + 16 i.  The
+// five wait states cover a scalar base written by a vector instruction.
+__device__ __forceinline__ void dma16_sbase(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+
+// Per-lane constants of one wave's work on the LDS ring: where its share of a
+// step's copy comes from and lands, and where its MFMA operands sit in a step
+// buffer.  A W-wave workgroup copies a step as 8 runs of 64 16-byte units
+// (1 KB) of keys and 8 of values; wave w copies runs w * 8/W .. (w+1) * 8/W - 1,
+// all within page page_of<W>(w) of the step.
+template <int W>
+struct RingLane {
+  static constexpr int kRuns = 8 / W;
+  uint32_t k_src[kRuns], v_src[kRuns];  // byte offsets within the source page
+  uint32_t k_lo, k_hi, v_ln;            // operand byte offsets within a step buffer
+  __device__ __forceinline__ RingLane(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < kRuns; ++i) {
+      const int pos = (64 * (kRuns * wave + i) + lane) & 255;  // unit within the page
+      const int c = pos >> 4, d = pos >> 1;
+      k_src[i] = static_cast<uint32_t>((c * 16 + pa::ring::kslot(c, pos & 15)) * 16);
+      v_src[i] = static_cast<uint32_t>((d * 2 + vhalf(d, pos & 1)) * 16);
+    }
+    // Row m of the K operand holds token krow(m) of the step (bits 2 and 3 of
+    // m swapped), so the 16 accumulator rows of lane (q, hh) are 8
+    // consecutive tokens of each page: the k-slots of the P^T operand.  Key
+    // chunk c = 2 kk + hh of token t sits in unit (t / 16) 256 + 16 c +
+    // (t % 16 ^ (c & 8)); the value half of dim d = 32 dt + m for tokens
+    // 8 hh .. 8 hh + 7 of page pg in unit 256 pg + 2 d + (hh ^ bit 3 of d).
+    const int m = lane & 31, hh = lane >> 5;
+    const int ktok = (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1);
+    k_lo = static_cast<uint32_t>(((ktok >> 4) * 256 + 16 * hh + (ktok & 15)) * 16);
+    k_hi = static_cast<uint32_t>(((ktok >> 4) * 256 + 16 * hh + ((ktok & 15) ^ 8)) * 16);
+    v_ln = kVBytes + static_cast<uint32_t>((2 * m + (hh ^ ((m >> 3) & 1))) * 16);
+  }
+  // K operand kk (chunks 2 kk + hh) of the step buffer at `b`
+  __device__ __forceinline__ uint4 k_op(const char* b, int kk) const {
+    return *reinterpret_cast<const uint4*>(b + (kk < 4 ? k_lo : k_hi) + 512 * kk);
+  }
+  // V^T operand (page pg, dims 32 dt ..) of the step buffer at `b`
+  __device__ __forceinline__ uint4 v_op(const char* b, int pg, int dt) const {
+    return *reinterpret_cast<const uint4*>(b + v_ln + 4096 * pg + 1024 * dt);
+  }
+};
+
+// Online softmax of one 32-token step for one lane (16 scores of its query
+// column, x[i] = token 16 (i / 8) + 8 hh + i % 8 of the step): bf16 weights
+// against the column's reference, the lane's sum of them, and the lazy move
+// of the reference.  o are the column's output accumulators.
+struct OnlineSoftmax {
+  float m_run = -INFINITY, l_run = 0.f, neg_m = 0.f;  // neg_m: -m_run, or 0 while it is -inf
+  bool have_ref = false;                              // wave-uniform
+
+  __device__ __forceinline__ void weights(const float (&x)[16], float scale_log2,
+                                          uint32_t (&pw)[8], float& ls) const {
+    float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const float p0 = pa::fast_exp2(fmaf(x[i], scale_log2, neg_m));
+      const float p1 = pa::fast_exp2(fmaf(x[i + 1], scale_log2, neg_m));
+      pw[i >> 1] = pa::pack_bf16x2(p0, p1);
+      if (i & 2) ls1 = pa::dot2_bf16(pw[i >> 1], kOnesBf16x2, ls1);
+      else ls0 = pa::dot2_bf16(pw[i >> 1], kOnesBf16x2, ls0);
+    }
+    ls = ls0 + ls1;
+  }
+
+  // Weights of a step into pw; adds their sum to l_run.  The reference of a
+  // column moves only when one of its weights would exceed 2^8 -- seen as a
+  // lane's sum of 16 weights above 2^8, so no row maximum is needed on the
+  // common path -- or before the first reference is set (wave-uniform
+  // decision).  Then the two halves of each column combine their maxima, O and
+  // l are rescaled, and the weights are recomputed.
+  __device__ __forceinline__ void step(const float (&x)[16], float scale_log2, uint32_t (&pw)[8],
+                                       pa::f32x16_t (&o)[4]) {
+    float ls;
+    weights(x, scale_log2, pw, ls);
+    if (!have_ref || __any(!(ls <= kMaxLaneSum))) {
+      const float m_new = fmaxf(m_run, swap32_max(max16(x)) * scale_log2);
+      const float alpha = pa::fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] *= alpha;
+      m_run = m_new;
+      neg_m = m_new == -INFINITY ? 0.f : -m_new;
+      have_ref = true;
+      weights(x, scale_log2, pw, ls);
+    }
+    l_run += ls;
+  }
+};
+
 // Workgroup `bid` of a grid of ceil(num_heads * num_seqs / 8) * 8 *
-// num_qtiles, W * 64 threads.  W waves per workgroup, NB blocks of 32 query
-// rows per wave (every K and V operand read from LDS feeds NB matrix products).
-// The body of one workgroup; `bid` takes the place of the block index.
-template <int W, int NB>
+// num_qtiles, W * 64 threads (num_qtiles = ceil(max chunk / (32 W))).  The
+// body of one workgroup; `bid` takes the place of the block index.
+template <int W>
 __device__ __forceinline__ void prefill_tile(
     uint32_t bid, StepBuf (&buf)[kRing], uint16_t* __restrict__ out,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ block_tables, int32_t max_blocks,
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ context_lens, int32_t num_seqs,
     int32_t num_heads, int32_t num_kv_heads, int32_t num_qtiles, float scale_log2) {
-  constexpr int kRowsPerWave = 32 * NB;
-  constexpr int kRowsPerWG = W * kRowsPerWave;
+  constexpr int kRowsPerWG = W * 32;
+  using RL = RingLane<W>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -117,161 +245,102 @@ __device__ __forceinline__ void prefill_tile(
   const int wg_last = first_pos + min(wg_row0 + kRowsPerWG, n_q) - 1;
   const int nsteps = wg_last / kStep + 1;         // steps covering tokens 0 .. wg_last
 
-  const int row0 = wg_row0 + wave * kRowsPerWave;
+  const int row0 = wg_row0 + wave * 32;
   const bool wave_active = row0 < n_q;
-  const int qn = lane & 31;   // this lane's query column within a block
+  const int qn = lane & 31;   // this lane's query column
   const int hh = lane >> 5;   // which half of the accumulator rows
-  const int wave_last = first_pos + min(row0 + kRowsPerWave, n_q) - 1;
+  const int wave_last = first_pos + min(row0 + 32, n_q) - 1;
   const int wave_first = first_pos + row0;
-  int my_pos[NB];
+  const int my_row = min(row0 + qn, n_q - 1);
+  const int my_pos = first_pos + my_row;
 
-  // Q^T operands: lane (qn, hh) holds dims 16*kk + 8*hh .. +7 of its query
-  // row in each block.
-  uint4 qreg[NB][8];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int my_row = min(row0 + 32 * b + qn, n_q - 1);
-    my_pos[b] = first_pos + my_row;
+  // Q^T operand: lane (qn, hh) holds dims 16 kk + 8 hh .. + 7 of its row.
+  uint4 qreg[8];
+  {
     const uint16_t* qrow = q + (static_cast<int64_t>(q0 + my_row) * num_heads + h) * kD + 8 * hh;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qreg[b][kk] = *reinterpret_cast<const uint4*>(qrow + 16 * kk);
+    for (int kk = 0; kk < 8; ++kk) qreg[kk] = *reinterpret_cast<const uint4*>(qrow + 16 * kk);
   }
-  // Consume the query registers here: otherwise their load waits land in the
-  // step loop, where (loads retiring in order) they would also drain every
-  // step copy in flight.
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      asm volatile("" : "+v"(qreg[b][kk].x), "+v"(qreg[b][kk].y), "+v"(qreg[b][kk].z),
-                   "+v"(qreg[b][kk].w));
 
+  // Block ids of this wave's page of each step, preloaded into lanes: lane i
+  // holds step i's and step 64 + i's.  Pages past the last needed token name
+  // logical block 0 (always valid): their scores are masked and their values
+  // weighted by 0.
   const int32_t* bt_row = block_tables + static_cast<int64_t>(s) * max_blocks;
-  const int64_t blk_stride = static_cast<int64_t>(num_kv_heads) * kPageElems;
-  const int64_t head_off = static_cast<int64_t>(g) * kPageElems;
-
-  // Pages past the last needed token load logical block 0 instead (always
-  // valid): their scores are masked, and their values must just be finite.
-  auto issue = [&](int step) {
-    const int lb = step * kPages + pa::ring::page_of<W>(wave);
-    pa::ring::issue_step<W>(buf[step % kRing], kc, vc, bt_row[lb * kBS <= wg_last ? lb : 0],
-                            blk_stride, head_off, wave, lane);
+  const int pw_page = pa::ring::page_of<W>(wave);
+  auto page_index = [&](int st) {
+    const int lb = st * kPages + pw_page;
+    return st < nsteps && lb * kBS <= wg_last ? lb : 0;
   };
-  // Values of tokens at or past L in the step's last page: zero them in LDS
-  // (the cache may hold NaN there, and 0 * NaN would reach every query).
-  auto zero_tail = [&](int step) {
-    StepBuf& B = buf[step % kRing];
+  const int ids_lo = bt_row[page_index(lane)];
+  const int ids_hi = bt_row[page_index(lane + 64)];
+  // Consume the query registers and block ids before the copies are issued:
+  // the compiler does not count the copies (inline asm), so a wait for these
+  // loads placed at their first use would drain every copy in flight.
 #pragma unroll
-    for (int r = 0; r < 512 / (W * 64); ++r) {
-      const int row = tid + W * 64 * r;   // (page, dim) row, 2 units each
-      const int page = row >> 7, d = row & 127;
-      const int tok0 = (step * kPages + page) * kBS;
-      uint4* vr = &B.v[page * 256 + d * 2];
+  for (int kk = 0; kk < 8; ++kk)
+    asm volatile("" : "+v"(qreg[kk].x), "+v"(qreg[kk].y), "+v"(qreg[kk].z), "+v"(qreg[kk].w));
+  asm volatile("" ::"v"(ids_lo), "v"(ids_hi));
+
+  const RL rl(wave, lane);
+  const int64_t page_bytes = static_cast<int64_t>(kPageElems) * 2;
+  const int64_t blk_bytes = static_cast<int64_t>(num_kv_heads) * page_bytes;
+  const int64_t head_bytes = static_cast<int64_t>(g) * page_bytes;
+  const uint32_t ring_lds = pa::ring::lds_addr(&buf[0]);
+  const char* lds = reinterpret_cast<const char*>(&buf[0]);
+  const char* kc_b = reinterpret_cast<const char*>(kc);
+  const char* vc_b = reinterpret_cast<const char*>(vc);
+  auto issue = [&](int step) {
+    const int phys = step < 64    ? __builtin_amdgcn_readlane(ids_lo, step)
+                     : step < 128 ? __builtin_amdgcn_readlane(ids_hi, step - 64)
+                                  : bt_row[page_index(step)];
+    const int64_t src = static_cast<int64_t>(phys) * blk_bytes + head_bytes;
+    const uint32_t dst = ring_lds + static_cast<uint32_t>(step % kRing) * kStepBytes;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int keep = L - (tok0 + 8 * half);
-        if (keep < 8) {
-          uint4& w4 = vr[vhalf(d, half)];
-          uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            w[i] &= (2 * i < keep ? 0x0000ffffu : 0u) | (2 * i + 1 < keep ? 0xffff0000u : 0u);
-          w4 = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-      }
+    for (int i = 0; i < RL::kRuns; ++i) {
+      const uint32_t u0 = 64u * static_cast<uint32_t>(RL::kRuns * wave + i);
+      dma16_sbase(kc_b + src, rl.k_src[i], dst + 16 * u0);
+      dma16_sbase(vc_b + src, rl.v_src[i], dst + kVBytes + 16 * u0);
     }
   };
 
-  pa::f32x16_t o[NB][4];
-  float m_run[NB], l_run[NB], neg_m[NB];  // neg_m: -m_run, or 0 while m_run is -inf
+  pa::f32x16_t o[4];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[b][i] = pa::f32x16_t{};
-    m_run[b] = -INFINITY;
-    l_run[b] = 0.f;
-    neg_m[b] = 0.f;
-  }
-
-  // Row m of the K operand (and of S^T) holds token krow(m) of the step: m
-  // with bits 2 and 3 swapped.  Then the 16 accumulator rows of lane (q, hh)
-  // -- rows 8*(j/4) + 4*hh + j%4 -- are tokens 16*(j/8) + 8*hh + j%8, i.e.
-  // 8 consecutive tokens of each page, exactly the k-slots 8*hh..8*hh+7 of
-  // the PV product's P^T operand; so the matching V^T operand is one 16-byte
-  // half row of the d-major value page.
-  const int m_row = lane & 31;
-  const int ktok = (m_row & 0x13) | ((m_row & 4) << 1) | ((m_row & 8) >> 1);
+  for (int i = 0; i < 4; ++i) o[i] = pa::f32x16_t{};
+  OnlineSoftmax sm;
 
   auto step_compute = [&](int step) {
-    const StepBuf& B = buf[step % kRing];
+    const char* b = lds + static_cast<uint32_t>(step % kRing) * kStepBytes;
     const int t0 = step * kStep;
-    // ---- S^T = K Q^T, each K operand feeding every block
-    pa::f32x16_t sa[NB];
+    // ---- S^T = K Q^T
+    pa::f32x16_t sa = pa::f32x16_t{};
 #pragma unroll
-    for (int b = 0; b < NB; ++b) sa[b] = pa::f32x16_t{};
+    for (int kk = 0; kk < 8; ++kk) sa = mfma32(rl.k_op(b, kk), qreg[kk], sa);
+    // ---- online softmax: lane (qn, hh) element i is token
+    // t0 + 16 (i / 8) + 8 hh + i % 8 of query row row0 + qn
+    float x[16];
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int c = 2 * kk + hh;
-      const uint4 a0 = B.k[((ktok >> 4) * 16 + c) * 16 + pa::ring::kslot(c, ktok & 15)];
+    for (int i = 0; i < 16; ++i) x[i] = sa[i];
+    const bool tail = t0 + kStep > L;
+    if (t0 + kStep - 1 > wave_first || tail) {  // diagonal or tail step
+      const int lim = min(my_pos, L - 1) - t0 - 8 * hh;  // keep offsets <= lim
 #pragma unroll
-      for (int b = 0; b < NB; ++b) sa[b] = mfma32(a0, qreg[b][kk], sa[b]);
+      for (int i = 0; i < 16; ++i)
+        if (16 * (i >> 3) + (i & 7) > lim) x[i] = -INFINITY;
     }
-    // ---- online softmax per block: lane (qn, hh) element j is token
-    // t0 + 16*(j/8) + 8*hh + j%8 of query row 32*b + qn
-    uint4 pb[NB][kPages];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      float x[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) x[j] = sa[b][j];
-      if (t0 + kStep - 1 > wave_first + 32 * b || t0 + kStep > L) {  // diagonal or tail step
-        const int lim = min(my_pos[b], L - 1) - t0 - 8 * hh;         // keep offsets <= lim
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int off = 16 * (j >> 3) + (j & 7);
-          if (off > lim) x[j] = -INFINITY;
-        }
-      }
-      float mx = fmaxf(x[0], x[1]);
-#pragma unroll
-      for (int j = 2; j < 16; j += 2) mx = fmaxf(mx, fmaxf(x[j], x[j + 1]));
-      // Lazy rescale, wave-uniform: only when some query's score exceeds its
-      // reference by more than 2^8 (scale > 0: max commutes with it).  Only
-      // then are the two halves of each query column combined.
-      if (__any(mx * scale_log2 > m_run[b] + kLazyRescale)) {
-        const float m_new = fmaxf(m_run[b], swap32_max(mx) * scale_log2);
-        const float alpha = pa::fast_exp2(m_run[b] - m_new);
-        l_run[b] *= alpha;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[b][i] *= alpha;
-        m_run[b] = m_new;
-        neg_m[b] = m_new == -INFINITY ? 0.f : -m_new;
-      }
-      uint32_t pw[8];
-      float ls = 0.f;
-#pragma unroll
-      for (int j = 0; j < 16; j += 2) {
-        const float p0 = pa::fast_exp2(fmaf(x[j], scale_log2, neg_m[b]));
-        const float p1 = pa::fast_exp2(fmaf(x[j + 1], scale_log2, neg_m[b]));
-        ls += p0 + p1;
-        pw[j >> 1] = pa::pack_bf16x2(p0, p1);
-      }
-      l_run[b] += ls;
-      // P^T operands, one per page: elements 8*pg .. 8*pg+7 are tokens
-      // 8*hh .. 8*hh+7 of page pg.
-#pragma unroll
-      for (int pg = 0; pg < kPages; ++pg)
-        pb[b][pg] = make_uint4(pw[4 * pg], pw[4 * pg + 1], pw[4 * pg + 2], pw[4 * pg + 3]);
-    }
-    // ---- O^T += V^T P^T, each V operand feeding every block
+    uint32_t pw[8];
+    sm.step(x, scale_log2, pw, o);
+    // ---- O^T += V^T P^T; values of tokens at or past L may be anything
+    // (0 * NaN): zeroed in registers
 #pragma unroll
     for (int pg = 0; pg < kPages; ++pg) {
+      const uint4 pb = make_uint4(pw[4 * pg], pw[4 * pg + 1], pw[4 * pg + 2], pw[4 * pg + 3]);
+      const int keep = L - (t0 + 16 * pg + 8 * hh);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const int d = dt * 32 + (lane & 31);
-        const uint4 va = B.v[pg * 256 + d * 2 + vhalf(d, hh)];
-#pragma unroll
-        for (int b = 0; b < NB; ++b) o[b][dt] = mfma32(va, pb[b][pg], o[b][dt]);
+        uint4 va = rl.v_op(b, pg, dt);
+        if (tail && keep < 8) va = keep_tokens(va, keep);
+        o[dt] = mfma32(va, pb, o[dt]);
       }
     }
   };
@@ -281,12 +350,6 @@ __device__ __forceinline__ void prefill_tile(
     // wait for this wave's copies of this step (later steps may stay in
     // flight), then for everyone's
     pa::ring::wait_step<kRing, W>(min(kRing - 2, nsteps - 1 - step));
-    if (step * kStep + kStep > L) {  // the step holding the sequence's last token
-      zero_tail(step);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-    }
     // the buffer written next was last read in the previous step, which every
     // wave has finished (barrier above)
     if (step + kRing - 1 < nsteps) issue(step + kRing - 1);
@@ -294,23 +357,20 @@ __device__ __forceinline__ void prefill_tile(
   }
 
   if (!wave_active) return;
+  const float lt = sm.l_run + __shfl_xor(sm.l_run, 32, 64);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const int row = row0 + qn;
+  if (row < n_q) {
+    uint16_t* orow = out + (static_cast<int64_t>(q0 + row) * num_heads + h) * kD;
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const float lt = l_run[b] + __shfl_xor(l_run[b], 32, 64);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const int row = row0 + 32 * b + qn;
-    if (row < n_q) {
-      uint16_t* orow = out + (static_cast<int64_t>(q0 + row) * num_heads + h) * kD;
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int jg = 0; jg < 4; ++jg) {
-          uint2 w;
-          w.x = pa::pack_bf16x2(o[b][dt][4 * jg] * inv, o[b][dt][4 * jg + 1] * inv);
-          w.y = pa::pack_bf16x2(o[b][dt][4 * jg + 2] * inv, o[b][dt][4 * jg + 3] * inv);
-          *reinterpret_cast<uint2*>(orow + dt * 32 + 8 * jg + 4 * hh) = w;
-        }
-    }
+      for (int jg = 0; jg < 4; ++jg) {
+        uint2 w;
+        w.x = pa::pack_bf16x2(o[dt][4 * jg] * inv, o[dt][4 * jg + 1] * inv);
+        w.y = pa::pack_bf16x2(o[dt][4 * jg + 2] * inv, o[dt][4 * jg + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + dt * 32 + 8 * jg + 4 * hh) = w;
+      }
   }
 }
 
