@@ -58,7 +58,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const int first = groups[3 * gi];
   const int count = min(min(groups[3 * gi + 1], kPrefixMembers), num_seqs - first);
   if (first < 0 || count <= 0) return;
-  const int P = split_begin(groups[3 * gi + 2], context_lens[first]);
+  const int P = split_begin(groups[3 * gi + 2], min(context_lens[first], max_blocks * kBS));
   const int part_start = part * partition;
   const int nq = count * gq_heads;
   const int q0 = chunk * Q;
@@ -115,7 +115,8 @@ int launch_decode(void* out, const void* q, const void* kc, const void* vc, cons
   }
   if (sp.slots > 1)
     hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(static_cast<uint32_t>(B) * H), dim3(64),
-                       0, st, static_cast<T*>(out), p, lens, H, sp.slots, partition, sp.rs);
+                       0, st, static_cast<T*>(out), p, lens, H, sp.slots, partition, sp.rs,
+                       max_blocks * BS);
   return pa_launch_status();
 }
 

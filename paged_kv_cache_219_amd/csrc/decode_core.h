@@ -165,7 +165,9 @@ __device__ __forceinline__ void decode_item(
 
   const int lane = threadIdx.x & 63;
   const int h0 = g * G;
-  const int L = context_lens[s];
+  // A length above the table row (a broken precondition) is cut to it, so no
+  // read leaves the row.
+  const int L = min(context_lens[s], max_blocks * BS);
   const int64_t out_row = (static_cast<int64_t>(s) * num_heads + h0) * D;
 
   if (L <= 0) {
@@ -475,18 +477,21 @@ __device__ __forceinline__ void decode_item(
 template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(
     T* __restrict__ out, Partials ws, const int32_t* __restrict__ context_lens, int32_t num_heads,
-    int32_t num_parts, int32_t partition, RangeSplit rs) {
+    int32_t num_parts, int32_t partition, RangeSplit rs, int32_t max_tokens) {
   constexpr int PER = D / 64;
   typedef float vec_t __attribute__((ext_vector_type(PER)));
   const int lane = threadIdx.x;
   const int64_t row = blockIdx.x;  // seq * num_heads + head
   const int s = static_cast<int>(row / num_heads);
-  const int L = context_lens[s];
+  const int L = min(context_lens[s], max_tokens);  // as the first pass cut it
   if (L <= 0) return;
   const int begin = rs.starts ? split_begin(rs.starts[s], L) : 0;
-  const int n_pre = rs.starts ? (begin + rs.pre_partition - 1) / rs.pre_partition : 0;
-  const int n_rest = (L - begin + partition - 1) / partition;
   const int part_base = rs.part_base;
+  // A length above the call's max_context_len (a broken precondition) would
+  // name partitions past the row's slots: read only the slots that exist.
+  const int n_pre = min(rs.starts ? (begin + rs.pre_partition - 1) / rs.pre_partition : 0,
+                        part_base);
+  const int n_rest = min((L - begin + partition - 1) / partition, num_parts - part_base);
   if (n_pre + n_rest <= 1) return;
   const int64_t row0 = row * num_parts;
   const float2* ml = reinterpret_cast<const float2*>(ws.ml) + row0;

@@ -240,7 +240,8 @@ __device__ __forceinline__ void mfma_decode_item(
   const int part = static_cast<int>(ps / static_cast<uint32_t>(num_seqs));
   if (part >= num_parts) return;
   const int G = num_heads / num_kv_heads;
-  const int L = context_lens[s];
+  // a length above the table row (a broken precondition) is cut to it
+  const int L = min(context_lens[s], max_blocks * kBS);
   const int64_t row0 = static_cast<int64_t>(s) * num_heads + static_cast<int64_t>(g) * G;
   if (L <= 0) {
     if (part == 0)

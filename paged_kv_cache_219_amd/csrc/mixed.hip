@@ -148,7 +148,7 @@ extern "C" int pa_mixed_step(void* out, const void* q, const void* k_cache, cons
                        static_cast<uint16_t*>(out) + row0, p,
                        context_lens + num_prefill_seqs, num_heads,
                        static_cast<int32_t>(dec_parts), dec_part,
-                       RangeSplit{nullptr, 0, dec_part});
+                       RangeSplit{nullptr, 0, dec_part}, max_blocks_per_seq * kBS);
   }
   return pa_launch_status();
 }

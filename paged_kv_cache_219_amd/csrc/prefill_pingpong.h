@@ -128,7 +128,8 @@ __device__ __forceinline__ void prefill_tile_pp(
   const int g = h / (num_heads / num_kv_heads);
   const int q0 = qsl[s];
   const int n_q = qsl[s + 1] - q0;
-  const int L = context_lens[s];
+  // a length above the table row (a broken precondition) is cut to it
+  const int L = min(context_lens[s], max_blocks * kBS);
   const int wg_row0 = qt * kRowsPP;
   if (wg_row0 >= n_q) return;  // whole workgroup idle (uniform: no barrier is skipped)
   const int first_pos = L - n_q;  // position of chunk row 0

@@ -49,7 +49,27 @@ def _dtype(t: torch.Tensor) -> int:
     return _DT[t.dtype]
 
 
+def _arg(dev: torch.device, name: str, t, dtype=None, contiguous: bool = True):
+    """Check one tensor argument before its address goes to libpa: a tensor on
+    the caches' device, of the given dtype, contiguous (with contiguous=False,
+    the caller's stride checks apply).  A host tensor's address would reach a
+    kernel as a device address."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor, got {type(t).__name__}")
+    if t.device != dev:
+        raise ValueError(f"{name} is on {t.device}; it must be on the caches' device {dev}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
 def _cache_dims(k_cache: torch.Tensor, v_cache: torch.Tensor):
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+    if v_cache.device != k_cache.device:
+        raise ValueError("k_cache and v_cache must be on one device")
     if k_cache.dim() != 5 or v_cache.dim() != 4:
         raise ValueError("k_cache must be 5-D and v_cache 4-D (libpa layout)")
     nb, kvh, dx, bs, x = k_cache.shape
@@ -77,6 +97,10 @@ def _check_tables(block_tables, context_lens, num_blocks, block_size):
 
 def pa_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, check_device_args=False):
     nb, kvh, d, bs = _cache_dims(k_cache, v_cache)
+    dev = k_cache.device
+    _arg(dev, "key", key, contiguous=False)
+    _arg(dev, "value", value, contiguous=False)
+    _arg(dev, "slot_mapping", slot_mapping, torch.int64)
     T = key.shape[0]
     if key.shape[1:] != (kvh, d) or value.shape[1:] != (kvh, d) or value.shape[0] != T:
         raise ValueError("key/value must be [T, num_kv_heads, head_dim]")
@@ -99,6 +123,7 @@ def pa_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, check_devic
 
 def pa_copy_blocks(k_cache, v_cache, pairs):
     nb, kvh, d, bs = _cache_dims(k_cache, v_cache)
+    _arg(k_cache.device, "pairs", pairs, torch.int32)
     if pairs.dtype != torch.int32 or pairs.dim() != 2 or pairs.shape[1] != 2 or not pairs.is_contiguous():
         raise ValueError("pairs must be contiguous int32 [n, 2]")
     check("pa_copy_blocks", lib().pa_copy_blocks(
@@ -122,6 +147,13 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float
     """``stream_kv``: PA_DECODE_STREAM_KV, for calls in which no block is read
     by two sequences (see include/pa.h)."""
     nb, kvh, d, bs = _cache_dims(k_cache, v_cache)
+    dev = k_cache.device
+    _arg(dev, "out", out)
+    _arg(dev, "q", q)
+    _arg(dev, "block_tables", block_tables, torch.int32)
+    _arg(dev, "context_lens", context_lens, torch.int32)
+    if workspace is not None:
+        _arg(dev, "workspace", workspace)
     B, H = q.shape[0], q.shape[1]
     if q.shape != (B, H, d) or out.shape != q.shape or not (q.is_contiguous() and out.is_contiguous()):
         raise ValueError("q/out must be contiguous [B, H, head_dim]")
@@ -184,6 +216,15 @@ def pa_decode_shared_prefix(out, q, k_cache, v_cache, block_tables, context_lens
     """pa_decode with prefix groups (device int32 tensors [G, 3] and [B], as
     pa_prefix_plan returns them)."""
     nb, kvh, d, bs = _cache_dims(k_cache, v_cache)
+    dev = k_cache.device
+    _arg(dev, "out", out)
+    _arg(dev, "q", q)
+    _arg(dev, "block_tables", block_tables, torch.int32)
+    _arg(dev, "context_lens", context_lens, torch.int32)
+    _arg(dev, "prefix_groups", prefix_groups, torch.int32)
+    _arg(dev, "seq_prefix_lens", seq_prefix_lens, torch.int32)
+    if workspace is not None:
+        _arg(dev, "workspace", workspace)
     B, H = q.shape[0], q.shape[1]
     if q.shape != (B, H, d) or out.shape != q.shape or not (q.is_contiguous() and out.is_contiguous()):
         raise ValueError("q/out must be contiguous [B, H, head_dim]")
@@ -241,6 +282,12 @@ def _check_groups(bt, lens, groups, pre, max_prefix_len, bs):
 def pa_prefill_chunk(out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens,
                      max_query_len: int, scale: float, check_device_args=False):
     nb, kvh, d, bs = _cache_dims(k_cache, v_cache)
+    dev = k_cache.device
+    _arg(dev, "out", out)
+    _arg(dev, "q", q)
+    _arg(dev, "block_tables", block_tables, torch.int32)
+    _arg(dev, "query_start_loc", query_start_loc, torch.int32)
+    _arg(dev, "context_lens", context_lens, torch.int32)
     T, H = q.shape[0], q.shape[1]
     B = context_lens.shape[0]
     if q.shape != (T, H, d) or out.shape != q.shape or not (q.is_contiguous() and out.is_contiguous()):
@@ -273,6 +320,14 @@ def pa_mixed_step(out, q, k_cache, v_cache, block_tables, query_start_loc, conte
     tokens (the rest, one query row each, after the chunks' rows) in one
     launch (plus the decode merge when partitioned)."""
     nb, kvh, d, bs = _cache_dims(k_cache, v_cache)
+    dev = k_cache.device
+    _arg(dev, "out", out)
+    _arg(dev, "q", q)
+    _arg(dev, "block_tables", block_tables, torch.int32)
+    _arg(dev, "query_start_loc", query_start_loc, torch.int32)
+    _arg(dev, "context_lens", context_lens, torch.int32)
+    if workspace is not None:
+        _arg(dev, "workspace", workspace)
     T, H = q.shape[0], q.shape[1]
     B = context_lens.shape[0]
     P = query_start_loc.shape[0] - 1

@@ -61,6 +61,17 @@ def test_wrong_gqa_head_map_is_caught(monkeypatch):
     _expect_failure(pins.test_decode_matches_torch_sdpa, "bf16")
 
 
+def test_wrong_head_map_in_decode_weights_is_caught(monkeypatch):
+    orig = attention.gather_kv
+
+    def bad_weights(q, k_cache, v_cache, bt, L, head, group, scale, dtype):
+        # query head h read against kv head h % KVH instead of h // group
+        K, _ = orig(k_cache, v_cache, bt, L, head % k_cache.shape[1], dtype)
+        return attention.softmax_weights(cache.to_f64(q, dtype), K, scale)
+    monkeypatch.setattr(attention, "decode_weights", bad_weights)
+    _expect_failure(pins.test_softmax_weights_sum_to_one)
+
+
 def test_causal_off_by_one_is_caught(monkeypatch):
     orig = attention.attend
 

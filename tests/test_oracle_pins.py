@@ -246,12 +246,18 @@ def test_softmax_weights_sum_to_one():
     st = run.build(sc)
     q = sc.q()
     tables, lens = run.batch_tables(st, sc)
+    ref = attention.decode(q, st.k_cache, st.v_cache, tables, lens, spec.scale, "bf16")
     for i in range(3):
         for h in range(4):
             p = attention.decode_weights(q[i, h], st.k_cache, st.v_cache, tables[i], lens[i], h, 2,
                                          spec.scale, "bf16")
             assert p.shape == (lens[i],) and np.all(p > 0)
             assert abs(p.sum() - 1.0) <= 1e-12
+            # the weights' head map: applied to the values of kv head h // 2
+            # (heads 0, 1 -> 0; 2, 3 -> 1) they give decode's row, which the
+            # SDPA pins fix independently
+            _, V = attention.gather_kv(st.k_cache, st.v_cache, tables[i], lens[i], h // 2, "bf16")
+            np.testing.assert_allclose(p @ V, ref[i, h], rtol=0, atol=1e-12)
 
 
 def test_physical_block_permutation_is_bit_invariant():
