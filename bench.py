@@ -34,6 +34,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+SCRUB_BYTES = 1 << 30  # written between timed kernel launches (the MALL is 256 MB)
+KERNEL_WARMUP = 10     # untimed scrubbed launches before the timed ones
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 METRIC = "decode KV-read GB/s (% HBM peak), seq-tokens/s; prefill-chunk TFLOP/s (% MFMA)"
 
@@ -150,9 +152,7 @@ def bench_decode(name: str, steps: int, warmup: int, grouped: bool = False):
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     kv_total = 0
-    uniq_total = 0
     ncow_total = 0
-    snap = []
     plan_groups = 0
     streamed = 0
     torch.cuda.synchronize()
@@ -195,18 +195,31 @@ def bench_decode(name: str, steps: int, warmup: int, grouped: bool = False):
         if timed:
             dec_ev[i - warmup][1].record(stream)
             kv_total += kv_bytes(lens, spec)
-            if name.startswith("shared_prefix"):
-                snap.append((tables.copy(), lens.copy()))  # accounted after timing
             ncow_total += len(cow)
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    for tables, lens in snap:
-        uniq_total += unique_kv_bytes(tables, lens, spec)
     step_ms = t0.elapsed_time(t1) / steps
-    dec_t = np.array([a.elapsed_time(b) for a, b in dec_ev])
-    dec_ms = float(np.mean(dec_t))
+    in_step_ms = float(np.mean([a.elapsed_time(b) for a, b in dec_ev]))
     kv_step = kv_total / steps
+
+    # The kernel alone: the last step's call again, timed launch by launch with
+    # a 1 GiB scrub written before each (outside the events), so no launch
+    # finds its pages in the caches; the median is the figure reported.
+    last_q = qs[total - 1]
+    if grouped:
+        def launch():
+            pa_decode_shared_prefix(out, last_q, w.k_cache, w.v_cache, d_tab, d_len, spec.scale,
+                                    spec.partition, int(lens.max()), d_grp[:ng], d_pre, max_pre,
+                                    ws, stream_kv=once)
+    else:
+        def launch():
+            pa_decode(out, last_q, w.k_cache, w.v_cache, d_tab, d_len, spec.scale, spec.partition,
+                      int(lens.max()), ws, stream_kv=once)
+    dec_t = scrubbed_launch_times(launch, steps, dev)
+    dec_ms = float(np.median(dec_t))
+    kv_last = kv_bytes(lens, spec)
+    uniq_last = unique_kv_bytes(tables, lens, spec)
     res = {
         "workload": name, "entry": "pa_decode_shared_prefix" if grouped else "pa_decode",
         "batch": B, "heads": spec.num_heads, "kv_heads": spec.num_kv_heads,
@@ -215,23 +228,48 @@ def bench_decode(name: str, steps: int, warmup: int, grouped: bool = False):
         "kv_bytes_per_step": kv_step,
         "step_kv_GBs": kv_step / (step_ms * 1e-3) / 1e9,
         "seq_tokens_per_s": B / (step_ms * 1e-3),
-        "decode_ms": dec_ms,
-        "decode_ms_median": float(np.median(dec_t)), "decode_ms_min": float(dec_t.min()),
-        "decode_ms_p90": float(np.percentile(dec_t, 90)),
-        "decode_kv_GBs": kv_step / (dec_ms * 1e-3) / 1e9,
+        # scrubbed launches of the last step's call: median (the figure), min, p90, mean
+        "decode_ms": dec_ms, "decode_ms_min": float(dec_t.min()),
+        "decode_ms_p90": float(np.percentile(dec_t, 90)), "decode_ms_mean": float(dec_t.mean()),
+        "decode_ms_in_step": in_step_ms,  # inside the step loop, mean
+        "launch_kv_bytes": kv_last,        # logical: every sequence's pages
+        "launch_unique_kv_bytes": uniq_last,  # each distinct page counted once
+        # HBM rate on the bytes the method must move (a shared page once)
+        "decode_kv_GBs": uniq_last / (dec_ms * 1e-3) / 1e9,
+        "decode_hbm_frac": uniq_last / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        # every sequence's pages counted: above HBM peak where pages are shared
+        "decode_effective_GBs": kv_last / (dec_ms * 1e-3) / 1e9,
+        "decode_effective_frac": kv_last / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "cow_pairs": ncow_total,
         "stream_kv_calls": int(streamed),
     }
     if grouped:
         res["prefix_groups"] = plan_groups
-    res["decode_hbm_frac"] = res["decode_kv_GBs"] / HBM_PEAK_GBS
-    if uniq_total:
-        res["unique_kv_bytes_per_step"] = uniq_total / steps
-        res["decode_unique_kv_GBs"] = uniq_total / steps / (dec_ms * 1e-3) / 1e9
-        res["decode_hbm_frac_unique"] = res["decode_unique_kv_GBs"] / HBM_PEAK_GBS
     del w, ks, vs, qs, ws
     torch.cuda.empty_cache()
     return res
+
+
+def scrubbed_launch_times(launch, n: int, dev) -> np.ndarray:
+    """Milliseconds of ``n`` launches of ``launch`` (after KERNEL_WARMUP
+    untimed ones), each preceded by a SCRUB_BYTES fill outside its HIP events
+    on the current stream."""
+    import torch
+    scrub = torch.empty(SCRUB_BYTES // 4, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for it in range(KERNEL_WARMUP + n):
+        scrub.fill_(it)
+        k = it - KERNEL_WARMUP
+        if k >= 0:
+            ev[k][0].record(stream)
+        launch()
+        if k >= 0:
+            ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    del scrub
+    return np.array([a.elapsed_time(b) for a, b in ev])
 
 
 def prefill_flops(cached, n_q, spec) -> float:
@@ -280,15 +318,22 @@ def bench_prefill(name: str, steps: int, warmup: int):
     t1.record(stream)
     torch.cuda.synchronize()
     step_ms = t0.elapsed_time(t1) / steps
-    pf_t = np.array([a.elapsed_time(b) for a, b in ev])
-    pf_ms = float(np.mean(pf_t))
+    in_step_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # the kernel alone, scrubbed launches; the median is the figure reported
+    pf_t = scrubbed_launch_times(
+        lambda: pa_prefill_chunk(out, q, w.k_cache, w.v_cache, bt, qsl, lens, max_q, spec.scale),
+        steps, dev)
+    pf_ms = float(np.median(pf_t))
     cached = sc.notes["cached"]
     flops = prefill_flops(cached, sc.query_lens, spec)
     res = {
         "workload": name, "seqs": len(sc.batch), "chunk": max_q, "heads": spec.num_heads,
         "head_dim": spec.head_dim, "cached_tokens": cached,
-        "ms_per_step": step_ms, "prefill_ms": pf_ms, "prefill_ms_median": float(np.median(pf_t)),
-        "prefill_ms_min": float(pf_t.min()), "prefill_ms_p90": float(np.percentile(pf_t, 90)),
+        "ms_per_step": step_ms,
+        # scrubbed launches: median (the figure), min, p90, mean
+        "prefill_ms": pf_ms, "prefill_ms_min": float(pf_t.min()),
+        "prefill_ms_p90": float(np.percentile(pf_t, 90)), "prefill_ms_mean": float(pf_t.mean()),
+        "prefill_ms_in_step": in_step_ms,  # right after the chunk's cache write, mean
         "flops_per_call": flops,
         "prefill_TFLOPs": flops / (pf_ms * 1e-3) / 1e12,
         "query_tokens_per_s": sum(sc.query_lens) / (step_ms * 1e-3),
@@ -518,39 +563,141 @@ def bench_block_sizes(steps: int, warmup: int):
             "partition": part, "kv_bytes": kvb, "rows": rows}
 
 
-def cpu_baseline(budget_s: float = 10.0, max_passes: int = 8):
-    """The fp64 numpy oracle decoding the headline workload's batch, four
-    sequences at a time, single-threaded (BLAS pinned to one thread).  The
-    cache is built once, untimed; whole passes over the batch repeat until
-    ``budget_s`` of attention time has accrued."""
+# ---------------------------------------------------------------------------
+# The oracle timed on the host cores (a reported baseline, not a target).
+#
+# Each config's sample is split over worker processes started fresh (spawn:
+# they inherit no GPU state and import no GPU library).  A worker builds the
+# oracle's cache for its own sequences (untimed: the cache write replays the
+# allocator script), waits at a barrier with the others, then runs the oracle
+# attention over its share and reports the elapsed time and the work done.
+# The all-core figure is the sample's work over the slowest worker's time.
+
+CPU_SAMPLES = {
+    # config: (sequences: "all" or every n-th, prefill rows: every n-th or None)
+    "tiny_decode_f32": ("all", None),
+    "decode_bf16": ("all", None),
+    "gqa_decode_bf16": (4, None),
+    "shared_prefix_bf16": (4, None),
+    "chunked_prefill_bf16": ("all", 16),
+}
+CPU_ONE_THREAD = ("tiny_decode_f32", "decode_bf16", "gqa_decode_bf16", "shared_prefix_bf16")
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _sample_seqs(sc, every):
+    idx = list(range(len(sc.batch)))
+    return idx if every == "all" else idx[::every]
+
+
+_BARRIER = None
+
+
+def _init_worker(barrier):
+    global _BARRIER
+    _BARRIER = barrier
+
+
+def _oracle_share(task):
+    """Worker: oracle attention over batch indices ``idx`` of config ``name``
+    (prefill: rows every ``row_every``), BLAS limited to one thread.  Returns
+    (seconds, kv bytes, flops, query rows)."""
+    name, idx, row_every = task
     from threadpoolctl import threadpool_limits
 
     from oracle import attention, run
     from synth import config_script
 
-    sc = config_script("decode_bf16")
+    sc = config_script(name)
     spec = sc.spec
-    st = run.build(sc)
-    tables, lens = run.batch_tables(st, sc)
+    st = run.build(sc, only_seqs=[sc.batch[i] for i in idx]) if idx else None
+    tables, lens = run.batch_tables(st, sc) if st else (None, None)
     q = sc.q(0)
-    B = len(sc.batch)
-    done_bytes, elapsed, passes = 0, 0.0, 0
+    if _BARRIER is not None:
+        _BARRIER.wait()
+    kvb = flops = rows = 0
+    t = time.perf_counter()
     with threadpool_limits(limits=1):
-        while elapsed < budget_s and passes < max_passes:
-            for start in range(0, B, 4):
-                idx = list(range(start, min(B, start + 4)))
-                t = time.perf_counter()
-                attention.decode(q[idx], st.k_cache, st.v_cache, tables[idx], lens[idx], spec.scale,
-                                 spec.dtype)
-                elapsed += time.perf_counter() - t
-                done_bytes += kv_bytes(lens[idx], spec)
-            passes += 1
-    return {"value": done_bytes / elapsed / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{passes} pass(es) of the fp64 numpy oracle over the headline workload's "
-                      f"decode step ({B} sequences x {spec.num_heads} heads, "
-                      f"{kv_bytes(lens, spec) / 1e6:.0f} MB of KV per pass), BLAS limited to 1 "
-                      f"thread; {elapsed:.1f} s of attention time",
-            "seq_tokens_per_s": B * passes / elapsed}
+        if idx and spec.kind == "decode":
+            attention.decode(q[idx], st.k_cache, st.v_cache, tables[idx], lens[idx], spec.scale,
+                             spec.dtype)
+            kvb = kv_bytes(lens[idx], spec)
+            rows = len(idx)
+        elif idx:
+            qsl = np.concatenate([[0], np.cumsum(sc.query_lens)]).astype(np.int32)
+            for i in idx:
+                r0, r1 = int(qsl[i]), int(qsl[i + 1])
+                sel = [(r, h) for r in range(r0, r1, row_every) for h in range(spec.num_heads)]
+                attention.prefill(q[r0:r1], st.k_cache, st.v_cache, tables[i:i + 1],
+                                  np.array([0, r1 - r0], np.int32), lens[i:i + 1], spec.scale,
+                                  spec.dtype, rows=[(r - r0, h) for r, h in sel])
+                pos0 = int(lens[i]) - (r1 - r0)
+                flops += sum(4.0 * spec.head_dim * (pos0 + (r - r0) + 1)
+                             for r, _ in sel)
+                rows += len(sel) // spec.num_heads
+    return time.perf_counter() - t, kvb, flops, rows
+
+
+def _run_shares(tasks, workers, timeout_s: float = 600.0):
+    import multiprocessing as mp
+    ctx = mp.get_context("spawn")
+    barrier = ctx.Barrier(len(tasks), timeout=timeout_s)  # a dead worker cannot hang the rest
+    with ctx.Pool(processes=len(tasks), initializer=_init_worker, initargs=(barrier,)) as pool:
+        return pool.map_async(_oracle_share, tasks, chunksize=1).get(timeout_s)
+
+
+def cpu_baseline(workers: int | None = None):
+    """The fp64 numpy oracle on the host: per config, its stated sample on
+    ``workers`` processes (default: the affinity cores, at most 16), and for
+    configs 1-4 the same sample on one process.  Rates are in each config's
+    unit: decode GB/s of KV read (and sequences/s), prefill TFLOP/s (and
+    query rows/s)."""
+    from synth import config_script
+
+    cores = len(os.sched_getaffinity(0))
+    workers = max(1, min(workers or cores, 16, cores))
+    rows_out = []
+    for name, (every, row_every) in CPU_SAMPLES.items():
+        sc = config_script(name)
+        idx = _sample_seqs(sc, every)
+        n = min(workers, len(idx))
+        shares = [idx[k::n] for k in range(n)]
+        res = _run_shares([(name, sh, row_every) for sh in shares], n)
+        t = max(r[0] for r in res)
+        kvb = sum(r[1] for r in res)
+        flops = sum(r[2] for r in res)
+        nrows = sum(r[3] for r in res)
+        row = {"workload": name, "processes": n, "seconds": t,
+               "sample": (f"{len(idx)} of {len(sc.batch)} sequences" +
+                          (f", every {row_every}th query row, all heads" if row_every else
+                           ", all heads"))}
+        if sc.spec.kind == "decode":
+            row.update(kv_GBs=kvb / t / 1e9, seqs_per_s=nrows / t, unit="GB/s")
+        else:
+            row.update(TFLOPs=flops / t / 1e12, query_rows_per_s=nrows / t, unit="TFLOP/s")
+        if name in CPU_ONE_THREAD:
+            (t1, kvb1, _, n1), = _run_shares([(name, idx, row_every)], 1)
+            row.update(one_thread_seconds=t1, one_thread_kv_GBs=kvb1 / t1 / 1e9)
+        rows_out.append(row)
+        print(f"[bench] cpu oracle {name}: {row['sample']} on {n} processes, {t:.2f} s" +
+              (f", 1 thread {row['one_thread_seconds']:.2f} s" if "one_thread_seconds" in row
+               else ""), file=sys.stderr, flush=True)
+    head = next(r for r in rows_out if r["workload"] == "decode_bf16")
+    return {"value": head["kv_GBs"], "unit": "GB/s", "cores": workers, "kind": "oracle",
+            "sample": f"the fp64 numpy oracle over the headline workload's decode step ("
+                      f"{head['sample']}) on {workers} worker processes, each BLAS-limited to one "
+                      f"thread; per-config samples and 1-thread times in 'configs'",
+            "cpu_model": cpu_model(), "affinity_cores": cores, "configs": rows_out}
 
 
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
@@ -764,10 +911,10 @@ def main():
             print(f"[bench] {name}: {r['prefill_ms']:.3f} ms = {r['prefill_TFLOPs']:.1f} TFLOP/s",
                   file=sys.stderr, flush=True)
         else:
-            extra = (f", unique {r['decode_unique_kv_GBs']:.0f} GB/s"
-                     if "decode_unique_kv_GBs" in r else "")
+            extra = (f" (effective {r['decode_effective_GBs']:.0f} GB/s)"
+                     if r["launch_kv_bytes"] != r["launch_unique_kv_bytes"] else "")
             print(f"[bench] {name}: decode {r['decode_ms']:.3f} ms = {r['decode_kv_GBs']:.0f} GB/s"
-                  f"{extra}", file=sys.stderr, flush=True)
+                  f" of unique KV{extra}", file=sys.stderr, flush=True)
         extras.append(r)
     copy = None if a.no_copy_calibration else copy_calibration()
     if copy:
@@ -798,8 +945,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": head["decode_kv_GBs"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": head["decode_kv_GBs"] / HBM_PEAK_GBS,
                      "traffic": measured_traffic(), "kernel": "pa_decode",
-                     "algorithmic_bytes_per_launch": head["kv_bytes_per_step"],
-                     "launch_ms": head["decode_ms"]},
+                     "algorithmic_bytes_per_launch": head["launch_unique_kv_bytes"],
+                     "launch_ms": head["decode_ms"],
+                     "launch_ms_is": f"median of {a.steps} launches, each after a "
+                                     f"{SCRUB_BYTES >> 20} MiB scrub"},
         "cpu_baseline": cpu,
         "copy_calibration": copy,
         "workloads": [head] + extras,
