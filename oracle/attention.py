@@ -26,24 +26,27 @@ from __future__ import annotations
 
 import numpy as np
 
-from .cache import read_key, read_value, to_f64
+from .cache import read_key_page, read_value_page, to_f64
 
 
 def gather_kv(k_cache, v_cache, block_table, context_len: int, kv_head: int, dtype: str):
     """Steps (1) and (2): K_s, V_s as float64 [L, head_dim], token t read from
-    physical block block_table[t // block_size] at offset t % block_size."""
+    physical block block_table[t // block_size] at offset t % block_size (a
+    whole page at a time, the last one cut at the context's end)."""
     block_size = k_cache.shape[3]
+    L = int(context_len)
     ks, vs = [], []
-    for t in range(int(context_len)):
-        phys = int(block_table[t // block_size])
+    for j in range(-(-L // block_size)):
+        phys = int(block_table[j])
         if phys < 0:
-            raise ValueError(f"position {t} maps to an unallocated logical block")
-        ks.append(read_key(k_cache, phys, kv_head, t % block_size))
-        vs.append(read_value(v_cache, phys, kv_head, t % block_size))
+            raise ValueError(f"position {j * block_size} maps to an unallocated logical block")
+        n = min(block_size, L - j * block_size)
+        ks.append(read_key_page(k_cache, phys, kv_head)[:n])
+        vs.append(read_value_page(v_cache, phys, kv_head)[:n])
     d = k_cache.shape[2] * k_cache.shape[4]
     if not ks:
         return np.zeros((0, d)), np.zeros((0, d))
-    return to_f64(np.stack(ks), dtype), to_f64(np.stack(vs), dtype)
+    return to_f64(np.concatenate(ks), dtype), to_f64(np.concatenate(vs), dtype)
 
 
 def softmax_weights(q: np.ndarray, K: np.ndarray, scale: float) -> np.ndarray:
@@ -122,6 +125,35 @@ def prefill(q, k_cache, v_cache, block_tables, query_start_loc, context_lens, sc
             for r, h in todo:
                 pos = L - n_q + (r - r0)
                 out[r, h] = attend(q64[r, h], K[: pos + 1], V[: pos + 1], scale)
+    return out
+
+
+def prefill_rows(q, k_cache, v_cache, block_tables, query_start_loc, context_lens, scale: float,
+                 dtype: str) -> np.ndarray:
+    """The same outputs as ``prefill`` for every row, computed a (sequence,
+    head) at a time in matrix form: S = scale * Q K^T over the chunk's rows,
+    entries with key position > query position set to -inf, a softmax per row,
+    then S V.  No blocking or online softmax: the definition with the rows of
+    a (sequence, head) stacked."""
+    q64 = to_f64(q, dtype)
+    Tq, H, D = q64.shape
+    kvh = k_cache.shape[1]
+    group = H // kvh
+    out = np.zeros((Tq, H, D))
+    for s in range(len(context_lens)):
+        r0, r1 = int(query_start_loc[s]), int(query_start_loc[s + 1])
+        n_q, L = r1 - r0, int(context_lens[s])
+        if n_q == 0:
+            continue
+        pos = L - n_q + np.arange(n_q)                  # position of each chunk row
+        masked = np.arange(L)[None, :] > pos[:, None]   # key after the query
+        for g in range(kvh):
+            K, V = gather_kv(k_cache, v_cache, block_tables[s], L, g, dtype)
+            for h in range(g * group, (g + 1) * group):
+                S = float(scale) * (q64[r0:r1, h] @ K.T)
+                S[masked] = -np.inf
+                P = np.exp(S - S.max(axis=1, keepdims=True))
+                out[r0:r1, h] = (P / P.sum(axis=1, keepdims=True)) @ V
     return out
 
 

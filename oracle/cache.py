@@ -73,6 +73,19 @@ def read_value(v_cache: np.ndarray, block: int, head: int, offset: int) -> np.nd
     return v_cache[block, head, :, offset]
 
 
+def read_key_page(k_cache: np.ndarray, block: int, head: int) -> np.ndarray:
+    """All key rows of one (block, head) page: [block_size, head_dim], row o
+    being read_key(k_cache, block, head, o)."""
+    page = k_cache[block, head]                      # [head_dim / X, block_size, X]
+    return page.transpose(1, 0, 2).reshape(page.shape[1], -1)
+
+
+def read_value_page(v_cache: np.ndarray, block: int, head: int) -> np.ndarray:
+    """All value rows of one (block, head) page: [block_size, head_dim], row o
+    being read_value(v_cache, block, head, o)."""
+    return v_cache[block, head].T
+
+
 def reshape_and_cache(key: np.ndarray, value: np.ndarray, k_cache: np.ndarray,
                       v_cache: np.ndarray, slot_mapping: np.ndarray) -> None:
     """Write new tokens' K/V into their cache slots, in place.
@@ -91,9 +104,9 @@ def reshape_and_cache(key: np.ndarray, value: np.ndarray, k_cache: np.ndarray,
         if slot < 0:
             continue
         b, o = int(slot) // block_size, int(slot) % block_size
-        for g in range(num_kv_heads):
-            k_cache[b, g, :, o, :] = key[i, g].reshape(head_dim // x, x)
-            v_cache[b, g, :, o] = value[i, g]
+        # every KV head of token i at once: head g, chunk c, element e
+        k_cache[b, :, :, o, :] = key[i].reshape(num_kv_heads, head_dim // x, x)
+        v_cache[b, :, :, o] = value[i]
 
 
 def copy_blocks(k_cache: np.ndarray, v_cache: np.ndarray, pairs) -> None:

@@ -32,7 +32,9 @@ def to_host_bits(t: torch.Tensor) -> np.ndarray:
 
 
 class DeviceWorkload:
-    def __init__(self, script, device="cuda", poison: bool = True, flush_tokens: int = 1 << 16):
+    def __init__(self, script, device="cuda", poison=True, flush_tokens: int = 1 << 16):
+        """``poison``: fill the pool before any write -- True: all-ones bits (NaN
+        in fp32 and bf16); a float: that value (e.g. +-1e4); False: leave it."""
         self.script = script
         self.spec = s = script.spec
         self.device = torch.device(device)
@@ -40,9 +42,12 @@ class DeviceWorkload:
         self.alloc = BlockAllocator(script.num_blocks, s.block_size, script.free_order)
         self.k_cache, self.v_cache = new_kv_cache(script.num_blocks, s.num_kv_heads, s.head_dim,
                                                   self.dtype, self.device, s.block_size)
-        if poison:  # all-ones bits: NaN in fp32 and bf16
+        if poison is True:  # all-ones bits: NaN in fp32 and bf16
             self.k_cache.view(torch.int16 if s.dtype == "bf16" else torch.int32).fill_(-1)
             self.v_cache.view(torch.int16 if s.dtype == "bf16" else torch.int32).fill_(-1)
+        elif poison is not False:
+            self.k_cache.fill_(float(poison))
+            self.v_cache.fill_(float(poison))
         self.cow_pairs: list = []
         self._flush_tokens = flush_tokens
         self._pending: list = []

@@ -1,72 +1,70 @@
 """GPU parity at the full workload sizes, in the launch configuration the
-benchmark times (each workload's default partition size).
+benchmark times (each workload's default partition size), over the whole
+output tensor.
 
-The whole pool and every block table are produced on both sides; the oracle
-writes and attends only over a sample of sequences (the first, the last, the
-shortest, the longest and four drawn at random), which is enough to check
-sampled outputs one by one.  Block tables are compared bit for bit for every
-sequence, the cache bit for bit on every slot the sampled sequences read.
+Both sides run the whole script: the block tables must agree bit for bit for
+every sequence, the whole K/V pool bit for bit (poisoned slots included), and
+every output within the stated tolerance (fp32: max abs <= 1e-5; bf16: max
+abs <= 2e-2 and relative L2 <= 5e-3 over the whole tensor).  The oracle is the
+plain definition; prefill uses its matrix form (attention.prefill_rows,
+pinned to the row-by-row oracle).  The script's K/V draws are made once and
+handed to both sides.
 """
 
 import numpy as np
 import pytest
 import torch
 
-from oracle import run
+from oracle import attention, run
 from synth import config_script
 
-from .parity import assert_close, gpu_step, oracle_step, raw_bits, say
-from paged_kv_cache_219_amd.workload import to_host_bits
+from .parity import assert_close, assert_pool_equal, gpu_step, say
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 
-def _sample_seqs(lens, k=4, seed=0):
-    lens = np.asarray(lens)
-    g = np.random.default_rng(seed)
-    pick = {0, len(lens) - 1, int(lens.argmin()), int(lens.argmax())}
-    pick |= set(int(x) for x in g.choice(len(lens), size=min(k, len(lens)), replace=False))
-    return sorted(pick)
+def memoize_draws(sc):
+    """Make the script hand out each append's K/V draw once (both sides use
+    the same seeded arrays; drawing them twice only costs time)."""
+    cache = {}
+    draw = sc.kv
+
+    def kv(op):
+        key = (op.stream, op.n)
+        if key not in cache:
+            cache[key] = draw(op)
+        return cache[key]
+    sc.kv = kv
+    return sc
+
+
+def whole_reference(sc, st):
+    s = sc.spec
+    tables, lens = run.batch_tables(st, sc)
+    q = sc.q(0)
+    if s.kind == "decode":
+        return attention.decode(q, st.k_cache, st.v_cache, tables, lens, s.scale, s.dtype)
+    qsl = np.concatenate([[0], np.cumsum(sc.query_lens)]).astype(np.int32)
+    return attention.prefill_rows(q, st.k_cache, st.v_cache, tables, qsl, lens, s.scale, s.dtype)
 
 
 @pytest.mark.parametrize("name", ["decode_bf16", "gqa_decode_bf16", "shared_prefix_bf16",
                                   "shared_prefix_bf16:grouped", "chunked_prefill_bf16"])
-def test_full_size_sampled(name):
-    say(f"full-size {name}: building on GPU")
+def test_full_size_whole_tensor(name):
+    say(f"full-size {name}: GPU step")
     name, _, mode = name.partition(":")
-    sc = config_script(name)
-    s = sc.spec
+    sc = memoize_draws(config_script(name))
     # grouped: through pa_decode_shared_prefix with the planner's default groups
     w, out, bt_h, lens_h = gpu_step(sc, shared_prefix=(8, 256) if mode else None)
     if mode:
         assert len(w.prefix_plan[0]) == len(sc.batch) // 8
-    assert torch.isfinite(out.float()).all()
-    seqs = _sample_seqs(lens_h)
-    g = np.random.default_rng(1)
-    if s.kind == "decode":
-        heads = sorted(set([0, s.num_heads - 1] + g.choice(s.num_heads, 4, replace=False).tolist()))
-        select = [(i, h) for i in seqs for h in heads]
-        rows = np.array([i for i, _ in select])
-    else:
-        qsl = np.concatenate([[0], np.cumsum(sc.query_lens)])
-        heads = [0, s.num_heads // 2, s.num_heads - 1]
-        select = []
-        for i in seqs[:4]:
-            for r in (0, 1, sc.query_lens[i] // 2, sc.query_lens[i] - 1):
-                select += [(int(qsl[i] + r), h) for h in heads]
-    say(f"  oracle on {len(select)} sampled outputs of sequences {seqs}")
-    st, ref = oracle_step(sc, select=select, only_seqs=[sc.batch[i] for i in seqs])
+    say("  oracle build (whole script)")
+    st = run.build(sc)
     tables, lens = run.batch_tables(st, sc)
     assert np.array_equal(bt_h, tables), "block tables differ from the oracle allocator"
     assert np.array_equal(lens_h, lens)
-    # cache: every block the sampled sequences read is bit-identical
-    gk, gv = to_host_bits(w.k_cache), to_host_bits(w.v_cache)
-    for i in seqs:
-        blocks = tables[i, : -(-int(lens[i]) // s.block_size)]
-        assert np.array_equal(raw_bits(gk[blocks]), raw_bits(st.k_cache[blocks]))
-        assert np.array_equal(raw_bits(gv[blocks]), raw_bits(st.v_cache[blocks]))
-    mask = np.zeros(out.shape[:2], bool)
-    for r, h in select:
-        mask[r, h] = True
-    mx, rel = assert_close(out, ref, s.dtype, mask=mask, what=name)
-    say(f"  max abs {mx:.2e} rel L2 {rel:.2e}")
+    assert_pool_equal(w, st)
+    say("  oracle attention (every output)")
+    ref = whole_reference(sc, st)
+    mx, rel = assert_close(out, ref, sc.spec.dtype, what=name)
+    say(f"  {out.numel() // sc.spec.head_dim} outputs: max abs {mx:.2e} rel L2 {rel:.2e}")

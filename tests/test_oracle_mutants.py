@@ -23,17 +23,47 @@ def _expect_failure(fn, *args, **kw):
 
 
 def test_transposed_key_layout_is_caught(monkeypatch):
-    def bad_read_key(k_cache, block, head, offset):
-        return k_cache[block, head, :, offset, :].T.reshape(-1)  # d = x * (D/X) + c
-    monkeypatch.setattr(attention, "read_key", bad_read_key)
+    def bad_read_key_page(k_cache, block, head):
+        return k_cache[block, head].reshape(k_cache.shape[3], -1)  # chunks not moved behind tokens
+    monkeypatch.setattr(attention, "read_key_page", bad_read_key_page)
     _expect_failure(pins.test_decode_matches_torch_sdpa, "bf16")
 
 
 def test_wrong_offset_in_gather_is_caught(monkeypatch):
-    def bad_read_value(v_cache, block, head, offset):
-        return v_cache[block, head, :, (offset + 1) % v_cache.shape[3]]
-    monkeypatch.setattr(attention, "read_value", bad_read_value)
+    def bad_read_value_page(v_cache, block, head):
+        return np.roll(v_cache[block, head].T, 1, axis=0)
+    monkeypatch.setattr(attention, "read_value_page", bad_read_value_page)
     _expect_failure(pins.test_decode_matches_torch_sdpa, "f32")
+
+
+def test_page_reader_off_by_one_is_caught(monkeypatch):
+    def bad(k_cache, block, head):
+        page = k_cache[block, head]
+        return np.roll(page.transpose(1, 0, 2).reshape(page.shape[1], -1), -1, axis=0)
+    monkeypatch.setattr(cache, "read_key_page", bad)
+    _expect_failure(pins.test_page_readers_match_row_readers)
+
+
+def test_prefill_rows_mask_off_by_one_is_caught(monkeypatch):
+    def bad_prefill_rows(q, k_cache, v_cache, block_tables, qsl, lens, scale, dtype):
+        q64 = cache.to_f64(q, dtype)
+        Tq, H, D = q64.shape
+        group = H // k_cache.shape[1]
+        out = np.zeros((Tq, H, D))
+        for s in range(len(lens)):
+            r0, r1 = int(qsl[s]), int(qsl[s + 1])
+            n_q, L = r1 - r0, int(lens[s])
+            pos = L - n_q + np.arange(n_q)
+            masked = np.arange(L)[None, :] >= pos[:, None]  # mistake: hides the query's own key
+            for h in range(H):
+                K, V = attention.gather_kv(k_cache, v_cache, block_tables[s], L, h // group, dtype)
+                S = float(scale) * (q64[r0:r1, h] @ K.T)
+                S[masked] = -np.inf
+                P = np.exp(S - S.max(axis=1, keepdims=True))
+                out[r0:r1, h] = np.nan_to_num(P / P.sum(axis=1, keepdims=True)) @ V
+        return out
+    monkeypatch.setattr(attention, "prefill_rows", bad_prefill_rows)
+    _expect_failure(pins.test_prefill_rows_matches_row_by_row)
 
 
 def test_dropped_scale_is_caught(monkeypatch):

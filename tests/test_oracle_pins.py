@@ -324,3 +324,36 @@ def test_partition_merge_equals_one_pass(partition):
         a = attention.attend(q, K, V, 0.9)
         b = attention.decode_partitioned(q, K, V, 0.9, partition)
         np.testing.assert_allclose(b, a, rtol=1e-12, atol=1e-14)
+
+
+# ------------------------------------------------ page readers, matrix-form prefill
+def test_page_readers_match_row_readers():
+    """read_key_page / read_value_page row o is the row read_key / read_value
+    return for offset o (pinned to the hand-worked layout by the golden test)."""
+    g = np.random.default_rng(11)
+    for dtype, x in (("bf16", 8), ("f32", 4)):
+        kc, vc = cache.empty_cache(3, 2, 16, 8, dtype)
+        raw = g.integers(0, 1 << 15, size=kc.size).astype(kc.dtype if dtype == "bf16" else np.float32)
+        kc[...] = raw.reshape(kc.shape)
+        vc[...] = g.integers(0, 1 << 15, size=vc.size).astype(vc.dtype).reshape(vc.shape)
+        for b in range(3):
+            for h in range(2):
+                kp, vp = cache.read_key_page(kc, b, h), cache.read_value_page(vc, b, h)
+                assert kp.shape == (8, 16) and vp.shape == (8, 16)
+                for o in range(8):
+                    assert np.array_equal(kp[o], cache.read_key(kc, b, h, o))
+                    assert np.array_equal(vp[o], cache.read_value(vc, b, h, o))
+
+
+def test_prefill_rows_matches_row_by_row():
+    """The matrix form over every row equals the per-row oracle (pinned to
+    SDPA) to 1e-12, for ragged chunks and grouped heads."""
+    spec = Spec("t", "prefill", 4, 2, 16, 4, "bf16")
+    sc = prefill_script(spec, [0, 5, 13], 7, seed=31)
+    st = run.build(sc)
+    tables, lens = run.batch_tables(st, sc)
+    q = sc.q()
+    qsl = np.concatenate([[0], np.cumsum(sc.query_lens)]).astype(np.int32)
+    ref = attention.prefill(q, st.k_cache, st.v_cache, tables, qsl, lens, spec.scale, "bf16")
+    got = attention.prefill_rows(q, st.k_cache, st.v_cache, tables, qsl, lens, spec.scale, "bf16")
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
