@@ -177,6 +177,30 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               size_t workspace_bytes, int32_t dtype, int32_t flags, void* stream);
 
 /*
+ * pa_decode_no_alloc -- pa_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same checks, kernels and results as pa_decode with
+ * the same arguments, but the split-context partials live in a device array
+ * inside the library (PA_NO_ALLOC_SCRATCH_BYTES, one copy per GPU, loaded
+ * with the library's code and held until the process ends) instead of a
+ * caller workspace.  No allocation or free is made by the call.
+ *
+ * A call whose partials (pa_decode_workspace_bytes with the same arguments)
+ * exceed PA_NO_ALLOC_SCRATCH_BYTES returns PA_ERR_WORKSPACE before any device
+ * work.  Nothing in the array needs to start at zero.  Every call on a GPU
+ * uses that GPU's one array: calls that may overlap in time on one GPU (two
+ * streams, or two threads) race and must be serialized by the caller.
+ * Returns PA_ERR_DEVICE if the array's address cannot be looked up.
+ */
+#define PA_NO_ALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+int pa_decode_no_alloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       int32_t num_blocks, float scale, int32_t partition,
+                       int32_t max_context_len, int32_t dtype, int32_t flags, void* stream);
+
+/*
  * Shared-prefix decode.  Sequences that share the physical blocks of a common
  * prefix -- the samples of one prompt (the skymod.tech overview on vLLM:
  * parallel sampling shares the prompt's memory), or requests whose prompts

@@ -43,6 +43,9 @@ _SIGS = {
     "pa_decode_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32, c_i32,
                           c_i32, c_i32, c_f32, c_i32, c_i32, c_vp, c_sz, c_i32, c_i32, c_vp]),
+    "pa_decode_no_alloc": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32,
+                                   c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_i32, c_i32, c_i32,
+                                   c_vp]),
     "pa_prefix_plan": (c_i32, [c_vp, c_i32, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp,
                                c_vp]),
     "pa_decode_shared_prefix_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),

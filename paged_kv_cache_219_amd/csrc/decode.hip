@@ -2,6 +2,8 @@
 // pa_decode / pa_decode_shared_prefix entry points.  The one-wave item body is
 // in decode_core.h.
 
+#include <mutex>
+
 #include "decode_core.h"
 #include "decode_mfma.h"
 
@@ -166,13 +168,14 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads,
   return ws_bytes(num_seqs, num_heads, head_dim, parts_for(max_context_len, partition));
 }
 
-extern "C" int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-                         const int32_t* block_tables, int32_t max_blocks_per_seq,
-                         const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
-                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                         int32_t num_blocks, float scale, int32_t partition,
-                         int32_t max_context_len, void* workspace, size_t workspace_bytes,
-                         int32_t dtype, int32_t flags, void* stream) {
+// pa_decode's checks and launches, on the workspace given.
+static int decode_call(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       int32_t num_blocks, float scale, int32_t partition,
+                       int32_t max_context_len, void* workspace, size_t workspace_bytes,
+                       int32_t dtype, int32_t flags, void* stream) {
   if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
   if (flags & ~PA_DECODE_STREAM_KV) return PA_ERR_INVALID_ARG;
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
@@ -216,6 +219,72 @@ extern "C" int pa_decode(void* out, const void* q, const void* k_cache, const vo
     default: return PA_DECODE_BS(16);
   }
 #undef PA_DECODE_BS
+}
+
+extern "C" int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int32_t num_blocks, float scale, int32_t partition,
+                         int32_t max_context_len, void* workspace, size_t workspace_bytes,
+                         int32_t dtype, int32_t flags, void* stream) {
+  return decode_call(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                     num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                     partition, max_context_len, workspace, workspace_bytes, dtype, flags,
+                     stream);
+}
+
+namespace {
+
+// The partials of pa_decode_no_alloc: a file-scope device array, one copy per
+// GPU, loaded with the library's code object and kept until the process ends.
+// Host code uses only the per-device address hipGetSymbolAddress returns (the
+// array's name on the host is a stand-in, not a device address).
+static __device__ __align__(256) unsigned char scratch[PA_NO_ALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of this GPU's copy of the scratch array (looked up once per
+// device, with that device current), or nullptr on failure.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" int pa_decode_no_alloc(void* out, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                  int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                  float scale, int32_t partition, int32_t max_context_len,
+                                  int32_t dtype, int32_t flags, void* stream) {
+  // The partials pa_decode would need (0 when no sequence can span two
+  // partitions) must fit the array: a larger call is refused before any
+  // device work.  Invalid arguments are reported by pa_decode's own checks.
+  const size_t need = pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len,
+                                                partition);
+  if (need > PA_NO_ALLOC_SCRATCH_BYTES) return PA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = device_scratch();
+    if (ws == nullptr) return PA_ERR_DEVICE;
+  }
+  return decode_call(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                     num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                     partition, max_context_len, ws, ws ? PA_NO_ALLOC_SCRATCH_BYTES : 0, dtype,
+                     flags, stream);
 }
 
 namespace {

@@ -180,6 +180,31 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float
         _flags(stream_kv), _stream(q)))
 
 
+def pa_decode_no_alloc(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                       partition: int, max_context_len: int, stream_kv: bool = False):
+    """pa_decode with the partials in the library's own device array: no
+    workspace, no allocation (see include/pa.h for the size limit and the rule
+    that overlapping calls on one GPU race)."""
+    nb, kvh, d, bs = _cache_dims(k_cache, v_cache)
+    dev = k_cache.device
+    _arg(dev, "out", out)
+    _arg(dev, "q", q)
+    _arg(dev, "block_tables", block_tables, torch.int32)
+    _arg(dev, "context_lens", context_lens, torch.int32)
+    B, H = q.shape[0], q.shape[1]
+    if q.shape != (B, H, d) or out.shape != q.shape:
+        raise ValueError("q/out must be [B, H, head_dim]")
+    if q.dtype != k_cache.dtype or out.dtype != q.dtype:
+        raise TypeError("q/out dtype must match the cache")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [B, max_blocks] and context_lens [B]")
+    check("pa_decode_no_alloc", lib().pa_decode_no_alloc(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(), B, H, kvh, d, bs,
+        nb, float(scale), int(partition), int(max_context_len), _dtype(q), _flags(stream_kv),
+        _stream(q)))
+
+
 def pa_prefix_plan(block_tables, context_lens, max_members: int = 8, min_prefix: int = 256,
                    block_size: int = BLOCK_SIZE):
     """Prefix groups of a batch (host arrays or tensors; runs on the host).
