@@ -339,6 +339,8 @@ def bench_prefill(name: str, steps: int, warmup: int):
         "query_tokens_per_s": sum(sc.query_lens) / (step_ms * 1e-3),
     }
     res["prefill_mfma_frac"] = res["prefill_TFLOPs"] / BF16_PEAK_TFLOPS
+    # rocprofv3 counters of this kernel (profiles/), while its sources are unchanged
+    res["counters"] = committed_counters("prefill") if name == "chunked_prefill_bf16" else None
     del w
     torch.cuda.empty_cache()
     return res
@@ -738,6 +740,20 @@ DECODE_SOURCES = ("paged_kv_cache_219_amd/csrc/decode.hip",
                   "paged_kv_cache_219_amd/csrc/pa_device.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pa_decode.decode_bf16.traffic.txt")
 CALIB_BYTES = 1 << 30  # copy_calibration's read (and write) size
+PREFILL_SOURCES = ("paged_kv_cache_219_amd/csrc/prefill.hip",
+                   "paged_kv_cache_219_amd/csrc/prefill_core.h",
+                   "paged_kv_cache_219_amd/csrc/prefill_pingpong.h",
+                   "paged_kv_cache_219_amd/csrc/page_ring.h",
+                   "paged_kv_cache_219_amd/csrc/pa_device.h")
+# per-kernel counter summaries: (profiles file, kernel name substring, sources)
+COUNTER_FILES = {
+    "prefill": (os.path.join(ROOT, "profiles", "pa_prefill_chunk.chunked_prefill_bf16.counters.txt"),
+                "prefill_chunk", PREFILL_SOURCES),
+    "gqa": (os.path.join(ROOT, "profiles", "pa_decode.gqa_decode_bf16.counters.txt"),
+            "decode", DECODE_SOURCES),
+}
+XCDS = 8             # GRBM_* counters are summed over the 8 XCDs
+SIMDS = 256 * 4      # 256 CUs x 4 SIMDs, one matrix core each
 
 
 def sources_sha256(paths=DECODE_SOURCES) -> str:
@@ -754,17 +770,32 @@ def sources_sha256(paths=DECODE_SOURCES) -> str:
     return h.hexdigest()
 
 
+def _at_lines(path):
+    try:
+        with open(path) as f:
+            return {k.strip(): v.strip() for k, v in
+                    (l.split(":", 1) for l in f.read().splitlines() if l.startswith("@"))}
+    except OSError:
+        return None
+
+
 def measured_traffic():
     """HBM bytes per pa_decode call from the committed counter summary, or
     None when the decode sources changed since the counters were taken."""
-    try:
-        with open(TRAFFIC_FILE) as f:
-            kv = dict(l.split(":", 1) for l in f.read().splitlines() if l.startswith("@"))
-    except OSError:
-        return None
-    if kv.get("@sources_sha256", "").strip() != sources_sha256():
+    kv = _at_lines(TRAFFIC_FILE)
+    if kv is None or kv.get("@sources_sha256", "") != sources_sha256():
         return None
     return float(kv["@traffic_bytes_per_call"])
+
+
+def committed_counters(key: str):
+    """The @ figures of a committed counter summary (COUNTER_FILES[key]) as
+    numbers, or None when its kernel sources changed since it was taken."""
+    path, _, sources = COUNTER_FILES[key]
+    kv = _at_lines(path)
+    if kv is None or kv.pop("@sources_sha256", "") != sources_sha256(sources):
+        return None
+    return {k[1:]: float(v) for k, v in kv.items()}
 
 
 def _read_csv(path):
@@ -836,6 +867,76 @@ def summarize_traffic(fetch_csv: str, write_csv: str) -> str:
     return "\n".join(lines)
 
 
+def summarize_counters(key: str, csv_paths) -> str:
+    """Per-dispatch means of every counter in the rocprofv3 --pmc runs
+    ``csv_paths`` for the kernels of COUNTER_FILES[key], with what follows
+    from them where the counters are there: the clock (GRBM_GUI_ACTIVE per
+    XCD over the dispatch's duration), the matrix cores' busy share
+    (SQ_VALU_MFMA_BUSY_CYCLES over SIMDs x cycles) and the HBM bytes
+    (FETCH_SIZE / WRITE_SIZE scaled by what they read for the same runs'
+    1 GiB device copy)."""
+    _, substr, sources = COUNTER_FILES[key]
+    per = {}     # (kernel, counter) -> values per dispatch
+    dur = {}     # kernel -> durations (ns) per dispatch, one per (run, dispatch)
+    copies = {}  # counter -> values of the copy dispatches
+    for path in csv_paths:
+        seen = set()
+        for r in _read_csv(path):
+            n, c, v = r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
+            if _is_copy(n):
+                copies.setdefault(c, []).append(v)
+                continue
+            if substr not in n:
+                continue
+            per.setdefault((n, c), []).append(v)
+            if (n, r["Dispatch_Id"]) not in seen:
+                seen.add((n, r["Dispatch_Id"]))
+                dur.setdefault(n, []).append(float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
+    def factor(ctr):
+        vals = copies.get(ctr, [])
+        vals = [v for v in vals if vals and v >= 0.25 * max(vals)]
+        return CALIB_BYTES / (1024.0 * float(np.mean(vals))) if vals else None
+    lines, at = [], {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        f = factor(ctr)
+        if f is not None:
+            lines.append(f"calibration: {ctr} of the 1 GiB device copy -> x{f:.3f} bytes per KiB count")
+    for n in sorted({n for n, _ in per}):
+        m = {c: float(np.mean(v)) for (k, c), v in per.items() if k == n}
+        d_ns = float(np.median(dur[n]))
+        lines.append(f"kernel {_short(n)}  ({len(dur[n])} dispatches over the runs, "
+                     f"median duration under counters {d_ns / 1e3:.1f} us)")
+        for c in sorted(m):
+            lines.append(f"  {c:32s} {m[c]:18.1f}")
+        tag = "decode_mfma" if "decode_mfma" in n else ("merge" if "merge" in n else
+                                                         _short(n).split("<")[0])
+        if "GRBM_GUI_ACTIVE" in m and d_ns >= 50e3:  # a short dispatch's window is mostly overhead
+            cycles = m["GRBM_GUI_ACTIVE"] / XCDS
+            ghz = cycles / d_ns
+            lines.append(f"  -> clock {ghz:.3f} GHz (GRBM_GUI_ACTIVE / {XCDS} XCDs / duration)")
+            at[f"{tag}_clock_ghz"] = ghz
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+                busy = m["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS * cycles)
+                lines.append(f"  -> matrix cores busy {busy:.3f} of the {SIMDS} SIMDs' cycles")
+                at[f"{tag}_mfma_busy_frac"] = busy
+        if "TCC_EA0_RDREQ_LEVEL" in m and m.get("TCC_EA0_RDREQ"):
+            lat = m["TCC_EA0_RDREQ_LEVEL"] / m["TCC_EA0_RDREQ"]
+            lines.append(f"  -> memory read latency {lat:.0f} cycles (TCC_EA0_RDREQ_LEVEL / TCC_EA0_RDREQ)")
+            at[f"{tag}_read_latency_cycles"] = lat
+            if "GRBM_GUI_ACTIVE" in m and d_ns >= 50e3:
+                infl = m["TCC_EA0_RDREQ_LEVEL"] / (m["GRBM_GUI_ACTIVE"] / XCDS)
+                lines.append(f"  -> {infl:.0f} read requests in flight at the memory, on average")
+                at[f"{tag}_reads_in_flight"] = infl
+        if "FETCH_SIZE" in m and "WRITE_SIZE" in m and factor("FETCH_SIZE") and factor("WRITE_SIZE"):
+            hbm = m["FETCH_SIZE"] * 1024 * factor("FETCH_SIZE") + m["WRITE_SIZE"] * 1024 * factor("WRITE_SIZE")
+            lines.append(f"  -> HBM bytes per dispatch {hbm / 1e6:.1f} MB (calibrated)")
+            at[f"{tag}_hbm_bytes"] = hbm
+    for k, v in at.items():
+        lines.append(f"@{k}: {v:.6g}")
+    lines.append(f"@sources_sha256: {sources_sha256(sources)}")
+    return "\n".join(lines)
+
+
 def run_workload(spec: str, steps: int, warmup: int):
     """``name`` or ``name:grouped`` (decode through pa_decode_shared_prefix)."""
     name, _, mode = spec.partition(":")
@@ -871,7 +972,16 @@ def main():
                     help="print a per-kernel table of a rocprofv3 --stats run and exit")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print calibrated HBM traffic of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar=("KERNELS", "CSV"),
+                    help="print per-kernel counters of rocprofv3 --pmc runs and exit; KERNELS "
+                         f"is one of {sorted(COUNTER_FILES)}")
     a = ap.parse_args()
+    if a.summarize_counters:
+        key, *paths = a.summarize_counters
+        if key not in COUNTER_FILES or not paths:
+            ap.error(f"--summarize-counters KERNELS CSV...; KERNELS in {sorted(COUNTER_FILES)}")
+        print(summarize_counters(key, paths))
+        return
     if a.summarize_stats:
         print(summarize_stats(a.summarize_stats))
         return
@@ -885,7 +995,10 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if a.only:
-        print(json.dumps(run_workload(a.only, a.steps, a.warmup)), flush=True)
+        r = run_workload(a.only, a.steps, a.warmup)
+        if not a.no_copy_calibration:  # a known copy, for counter runs of this workload
+            r["copy_calibration"] = copy_calibration()
+        print(json.dumps(r), flush=True)
         return
     head = bench_decode("decode_bf16", a.steps, a.warmup)
     print(f"[bench] decode_bf16: step {head['ms_per_step']:.3f} ms, decode {head['decode_ms']:.3f} ms "

@@ -57,3 +57,33 @@ def test_blocks_read_once_sees_shared_and_grouped_pages():
     assert bench.blocks_read_once(t, g, np.array([32, 32, 0]), 16)    # grouped: prefix read once
     g = np.array([[0, 2, 16]])
     assert not bench.blocks_read_once(t, g, np.array([16, 16, 0]), 16)  # block 2 outside prefix
+
+
+def test_counter_summary_derives_clock_busy_share_and_bytes(tmp_path):
+    cols = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp",
+            "End_Timestamp"]
+    k = "void (anonymous namespace)::prefill_chunk_pp_kernel(int)"
+    copy = "__amd_rocclr_copyBuffer"
+    # one 100 us dispatch at 2 GHz on each of 8 XCDs: 200k cycles per XCD
+    runs = {
+        "sq": [("1", k, "GRBM_GUI_ACTIVE", 8 * 200000), ("1", k, "SQ_VALU_MFMA_BUSY_CYCLES",
+                                                          1024 * 200000 // 4)],
+        "fetch": [("1", copy, "FETCH_SIZE", 524288), ("2", k, "FETCH_SIZE", 1000)],
+        "write": [("1", copy, "WRITE_SIZE", 1048576), ("2", k, "WRITE_SIZE", 10)],
+    }
+    paths = []
+    for name, rs in runs.items():
+        p = tmp_path / f"{name}.csv"
+        with open(p, "w", newline="") as f:
+            w = csv.writer(f)
+            w.writerow(cols)
+            for d, kn, c, v in rs:
+                w.writerow([d, kn, c, v, 1_000_000, 1_100_000])
+        paths.append(str(p))
+    text = bench.summarize_counters("prefill", paths)
+    at = {l.split(":")[0]: float(l.split(":")[1]) for l in text.splitlines()
+          if l.startswith("@") and "sha256" not in l}
+    assert abs(at["@prefill_chunk_pp_kernel_clock_ghz"] - 2.0) < 1e-9
+    assert abs(at["@prefill_chunk_pp_kernel_mfma_busy_frac"] - 0.25) < 1e-9
+    assert at["@prefill_chunk_pp_kernel_hbm_bytes"] == 1000 * 1024 * 2 + 10 * 1024
+    assert "@sources_sha256: " + bench.sources_sha256(bench.PREFILL_SOURCES) in text
