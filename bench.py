@@ -584,6 +584,7 @@ CPU_SAMPLES = {
     "chunked_prefill_bf16": ("all", 16),
 }
 CPU_ONE_THREAD = ("tiny_decode_f32", "decode_bf16", "gqa_decode_bf16", "shared_prefix_bf16")
+CPU_MIN_SECONDS = 1.5  # each worker repeats its share in whole passes for at least this long
 
 
 def cpu_model() -> str:
@@ -612,8 +613,9 @@ def _init_worker(barrier):
 
 def _oracle_share(task):
     """Worker: oracle attention over batch indices ``idx`` of config ``name``
-    (prefill: rows every ``row_every``), BLAS limited to one thread.  Returns
-    (seconds, kv bytes, flops, query rows)."""
+    (prefill: rows every ``row_every``), BLAS limited to one thread, repeated
+    in whole passes for at least CPU_MIN_SECONDS.  Returns (seconds, kv bytes,
+    flops, query rows, passes), the counts summed over the passes."""
     name, idx, row_every = task
     from threadpoolctl import threadpool_limits
 
@@ -627,27 +629,31 @@ def _oracle_share(task):
     q = sc.q(0)
     if _BARRIER is not None:
         _BARRIER.wait()
-    kvb = flops = rows = 0
+    kvb = flops = rows = passes = 0
     t = time.perf_counter()
     with threadpool_limits(limits=1):
-        if idx and spec.kind == "decode":
-            attention.decode(q[idx], st.k_cache, st.v_cache, tables[idx], lens[idx], spec.scale,
-                             spec.dtype)
-            kvb = kv_bytes(lens[idx], spec)
-            rows = len(idx)
-        elif idx:
-            qsl = np.concatenate([[0], np.cumsum(sc.query_lens)]).astype(np.int32)
-            for i in idx:
-                r0, r1 = int(qsl[i]), int(qsl[i + 1])
-                sel = [(r, h) for r in range(r0, r1, row_every) for h in range(spec.num_heads)]
-                attention.prefill(q[r0:r1], st.k_cache, st.v_cache, tables[i:i + 1],
-                                  np.array([0, r1 - r0], np.int32), lens[i:i + 1], spec.scale,
-                                  spec.dtype, rows=[(r - r0, h) for r, h in sel])
-                pos0 = int(lens[i]) - (r1 - r0)
-                flops += sum(4.0 * spec.head_dim * (pos0 + (r - r0) + 1)
-                             for r, _ in sel)
-                rows += len(sel) // spec.num_heads
-    return time.perf_counter() - t, kvb, flops, rows
+        while idx:
+            if spec.kind == "decode":
+                attention.decode(q[idx], st.k_cache, st.v_cache, tables[idx], lens[idx],
+                                 spec.scale, spec.dtype)
+                kvb += kv_bytes(lens[idx], spec)
+                rows += len(idx)
+            else:
+                qsl = np.concatenate([[0], np.cumsum(sc.query_lens)]).astype(np.int32)
+                for i in idx:
+                    r0, r1 = int(qsl[i]), int(qsl[i + 1])
+                    sel = [(r, h) for r in range(r0, r1, row_every) for h in range(spec.num_heads)]
+                    attention.prefill(q[r0:r1], st.k_cache, st.v_cache, tables[i:i + 1],
+                                      np.array([0, r1 - r0], np.int32), lens[i:i + 1], spec.scale,
+                                      spec.dtype, rows=[(r - r0, h) for r, h in sel])
+                    pos0 = int(lens[i]) - (r1 - r0)
+                    flops += sum(4.0 * spec.head_dim * (pos0 + (r - r0) + 1)
+                                 for r, _ in sel)
+                    rows += len(sel) // spec.num_heads
+            passes += 1
+            if time.perf_counter() - t >= CPU_MIN_SECONDS:
+                break
+    return time.perf_counter() - t, kvb, flops, rows, passes
 
 
 def _run_shares(tasks, workers, timeout_s: float = 600.0):
@@ -680,16 +686,20 @@ def cpu_baseline(workers: int | None = None):
         flops = sum(r[2] for r in res)
         nrows = sum(r[3] for r in res)
         row = {"workload": name, "processes": n, "seconds": t,
+               "passes_per_process": [int(r[4]) for r in res],
                "sample": (f"{len(idx)} of {len(sc.batch)} sequences" +
                           (f", every {row_every}th query row, all heads" if row_every else
-                           ", all heads"))}
+                           ", all heads") +
+                          f", split over the processes, each repeating its share in whole "
+                          f"passes for at least {CPU_MIN_SECONDS} s")}
         if sc.spec.kind == "decode":
             row.update(kv_GBs=kvb / t / 1e9, seqs_per_s=nrows / t, unit="GB/s")
         else:
             row.update(TFLOPs=flops / t / 1e12, query_rows_per_s=nrows / t, unit="TFLOP/s")
         if name in CPU_ONE_THREAD:
-            (t1, kvb1, _, n1), = _run_shares([(name, idx, row_every)], 1)
-            row.update(one_thread_seconds=t1, one_thread_kv_GBs=kvb1 / t1 / 1e9)
+            (t1, kvb1, _, n1, p1), = _run_shares([(name, idx, row_every)], 1)
+            row.update(one_thread_seconds=t1, one_thread_passes=int(p1),
+                       one_thread_kv_GBs=kvb1 / t1 / 1e9)
         rows_out.append(row)
         print(f"[bench] cpu oracle {name}: {row['sample']} on {n} processes, {t:.2f} s" +
               (f", 1 thread {row['one_thread_seconds']:.2f} s" if "one_thread_seconds" in row

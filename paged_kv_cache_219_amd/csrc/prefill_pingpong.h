@@ -21,18 +21,19 @@
 // kind, so the two phases are balanced by instruction count, not by unit: the
 // matrix phase, which issues only 16 MFMAs in its 512 cycles, also issues the
 // LDS reads of the next phase's operands (into the registers the products
-// before them have read) and the copies into the LDS ring; the softmax phase
-// is the softmax alone.  Addresses are per-lane constants plus a
-// scalar per step, block ids are preloaded into lanes, and the row sums come
-// from v_dot2 on the bf16 weights.
+// before them have read); the softmax phase issues this wave's share of a
+// ring copy and runs the softmax.  Addresses are per-lane constants plus a
+// scalar per step, block ids come from scalar loads a phase ahead, and the
+// row sums come from v_dot2 on the bf16 weights.
 //
 // Per wave, step j of the keys/values (32 tokens = two 16-token pages):
 //   matrix phase j:  O^T += V_{j-1}^T P_{j-1}^T   (8 x v_mfma_f32_32x32x16_bf16)
 //                    S^T  = K_j Q^T               (8 more)
 //                    with the LDS reads of V_j and K_{j+1} (operands of matrix
-//                    phase j + 1) between them, and this wave's share of the
-//                    copy of step j + kRingPP - 1 into the LDS ring;
-//   softmax phase j: online softmax of S_j -> P_j (bf16, in registers).
+//                    phase j + 1) between them;
+//   softmax phase j: this wave's share of the copy of step j + kRingPP - 1
+//                    into the LDS ring, then the online softmax of S_j -> P_j
+//                    (bf16, in registers).
 // The transposed form and the token order of the K operand's rows are those of
 // the 128-row kernel (prefill_core.h): each lane owns one query column, so the
 // softmax of a query stays in two lanes and P^T is built from the lane's own
@@ -48,8 +49,8 @@
 // At the end of its matrix phase j every wave waits for its own copy of step
 // j + 2, so the barrier after group 1's matrix phase j publishes step j + 2
 // before group 0's matrix phase j + 1 reads it.  The copy of step j + kRingPP
-// - 1, issued in matrix phase j, overwrites step j - 1, whose last reader was
-// group 1's matrix phase j - 1.
+// - 1, issued in softmax phase j, overwrites step j - 1, whose last reader was
+// group 1's matrix phase j - 1 (before the barrier that started the phase).
 #pragma once
 
 #include "prefill_core.h"

@@ -50,6 +50,7 @@ def test_every_wrapper_refuses_host_tensors(no_library):
         lambda: K.pa_reshape_and_cache(q, q, kc, vc, torch.zeros(2, dtype=torch.int64)),
         lambda: K.pa_copy_blocks(kc, vc, torch.zeros((1, 2), dtype=torch.int32)),
         lambda: K.pa_decode(out, q, kc, vc, bt, lens, 0.1, 0, 32),
+        lambda: K.pa_decode_no_alloc(out, q, kc, vc, bt, lens, 0.1, 0, 32),
         lambda: K.pa_decode_shared_prefix(out, q, kc, vc, bt, lens, 0.1, 0, 32,
                                           torch.zeros((1, 3), dtype=torch.int32), lens, 16),
         lambda: K.pa_prefill_chunk(out, q, kc, vc, bt, qsl, lens, 1, 0.1),
