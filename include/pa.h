@@ -68,8 +68,8 @@ typedef enum {
 typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
 
 /*
- * Flags of the decode entry points (pa_decode, pa_decode_shared_prefix,
- * pa_mixed_step).  PA_DECODE_STREAM_KV: read the K/V pages with the
+ * Flags of the decode entry points (pa_decode, pa_decode_no_alloc,
+ * pa_decode_shared_prefix, pa_mixed_step).  PA_DECODE_STREAM_KV: read the K/V pages with the
  * non-temporal hint.  Pass it when no physical block is read by more than one
  * sequence of the call (the allocator's reference counts tell the caller):
  * each page is then read once per call, and the hint keeps those reads from
@@ -77,10 +77,30 @@ typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
  * Leave it out when sequences of the call share blocks (forked samples,
  * matched prompt prefixes read through pa_decode): their repeat reads of a
  * shared page are served from the caches only without it (measured 42% slower
- * with it on 8 samples per prompt).  Results are the same either way.  Other
- * bits are reserved and must be 0 (PA_ERR_INVALID_ARG).
+ * with it on 8 samples per prompt).  Results are the same either way.
+ *
+ * PA_DECODE_FIND_SHARED (pa_decode and pa_decode_no_alloc only; bf16,
+ * head_dim 128, block_size 16, else PA_ERR_UNSUPPORTED): the call finds
+ * shared prefixes itself, on the device, and reads their pages once per group
+ * as pa_decode_shared_prefix does (deep-dive page, section "Cơ chế APC", item
+ * 2: requests with a matching prefix link the same physical blocks; the
+ * skymod.tech overview on vLLM: the samples of a prompt share its blocks).
+ * The batch is cut into aligned runs of PA_PREFIX_MAX_MEMBERS sequences; in
+ * each run, the first sequence leads a group that the following sequences
+ * join, in order, by the rule of pa_prefix_plan with min_prefix =
+ * PA_FIND_SHARED_MIN_PREFIX tokens (leading block ids in common with the
+ * leader, within both contexts' whole blocks, the page reads saved not
+ * falling).  Sharing that crosses a run boundary is read once per run.  The
+ * workspace must hold pa_decode_workspace_bytes_flags(..., flags) bytes.
+ * Results are those of pa_decode to fp32 rounding (the shared pages' partials
+ * are merged with the rest by the same log-sum-exp weights).  Pass
+ * PA_DECODE_STREAM_KV with it when no block is read by two groups or by a
+ * group and a sequence outside it.  Other bits are reserved and must be 0
+ * (PA_ERR_INVALID_ARG).
  */
 #define PA_DECODE_STREAM_KV 1
+#define PA_DECODE_FIND_SHARED 2
+#define PA_FIND_SHARED_MIN_PREFIX 256
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* pa_status_str(int status);
@@ -138,6 +158,18 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t he
                                  int32_t max_context_len, int32_t partition);
 
 /*
+ * pa_decode_workspace_bytes_flags -- device workspace of pa_decode called
+ * with `flags`: pa_decode_workspace_bytes without PA_DECODE_FIND_SHARED; with
+ * it, the partials of a prefix of up to max_context_len tokens and of the
+ * rest (as pa_decode_shared_prefix_workspace_bytes with max_prefix_len =
+ * max_context_len) plus the groups found: 4 bytes per sequence and 12 per run
+ * of PA_PREFIX_MAX_MEMBERS sequences, 256-byte aligned.
+ */
+size_t pa_decode_workspace_bytes_flags(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                       int32_t max_context_len, int32_t partition,
+                                       int32_t flags);
+
+/*
  * pa_decode -- one query token per sequence against its paged context.
  *
  * For sequence s and query head h (kv head g = h / (num_heads/num_kv_heads)),
@@ -161,10 +193,13 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t he
  *                  merges with log-sum-exp weights.
  *   max_context_len  host upper bound of context_lens (sizes the grid).
  *   workspace      device scratch of at least pa_decode_workspace_bytes(...)
- *                  bytes (may be NULL when that is 0); contents on entry are
- *                  ignored, contents on exit are unspecified.  Calls that
- *                  overlap in time must not share a workspace.
- *   flags          0 or PA_DECODE_STREAM_KV (see there).
+ *                  bytes (pa_decode_workspace_bytes_flags(...) with
+ *                  PA_DECODE_FIND_SHARED; may be NULL when that is 0);
+ *                  contents on entry are ignored, contents on exit are
+ *                  unspecified.  Calls that overlap in time must not share a
+ *                  workspace.
+ *   flags          0, PA_DECODE_STREAM_KV, PA_DECODE_FIND_SHARED, or both
+ *                  (see there).
  * Deterministic: the merge runs in partition order and the reduction order
  * depends only on logical positions, so results do not depend on block
  * placement, on which blocks are shared, or on scheduling.
@@ -185,8 +220,8 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
  * with the library's code and held until the process ends) instead of a
  * caller workspace.  No allocation or free is made by the call.
  *
- * A call whose partials (pa_decode_workspace_bytes with the same arguments)
- * exceed PA_NO_ALLOC_SCRATCH_BYTES returns PA_ERR_WORKSPACE before any device
+ * A call whose partials (pa_decode_workspace_bytes_flags with the same
+ * arguments) exceed PA_NO_ALLOC_SCRATCH_BYTES returns PA_ERR_WORKSPACE before any device
  * work.  Nothing in the array needs to start at zero.  Every call on a GPU
  * uses that GPU's one array: calls that may overlap in time on one GPU (two
  * streams, or two threads) race and must be serialized by the caller.

@@ -23,6 +23,8 @@ PA_OK = 0
 PA_F32 = 0
 PA_BF16 = 1
 PA_DECODE_STREAM_KV = 1
+PA_DECODE_FIND_SHARED = 2
+PA_FIND_SHARED_MIN_PREFIX = 256
 STATUS = {0: "PA_OK", -1: "PA_ERR_INVALID_ARG", -2: "PA_ERR_NO_FREE_BLOCKS",
           -3: "PA_ERR_UNKNOWN_SEQ", -4: "PA_ERR_SEQ_EXISTS", -5: "PA_ERR_UNSUPPORTED",
           -6: "PA_ERR_WORKSPACE", -7: "PA_ERR_DEVICE"}
@@ -41,6 +43,7 @@ _SIGS = {
                                      c_i32, c_i32, c_i32, c_i32, c_vp]),
     "pa_copy_blocks": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
     "pa_decode_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
+    "pa_decode_workspace_bytes_flags": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32, c_i32,
                           c_i32, c_i32, c_f32, c_i32, c_i32, c_vp, c_sz, c_i32, c_i32, c_vp]),
     "pa_decode_no_alloc": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32,
@@ -90,8 +93,9 @@ def header_functions(path: str = HEADER) -> list[str]:
 # The ABI this binding marshals for (include/pa.h, pa_version).  Version 2
 # added the `flags` argument before `stream` in pa_decode,
 # pa_decode_shared_prefix and pa_mixed_step: a version-1 library called with
-# these argument types takes the flags as its stream.
-ABI_VERSION = 2
+# these argument types takes the flags as its stream.  Version 3 added
+# pa_decode_workspace_bytes_flags and the PA_DECODE_FIND_SHARED flag.
+ABI_VERSION = 3
 
 
 def load_library(path: str, host_only: bool = False) -> ctypes.CDLL:

@@ -520,6 +520,6 @@ const char* pa_status_str(int status) {
   }
 }
 
-int pa_version(void) { return 2; }
+int pa_version(void) { return 3; }
 
 }  // extern "C"

@@ -86,6 +86,57 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 }
 
 
+// Prefix groups found on the device (PA_DECODE_FIND_SHARED): one wave per
+// aligned run of kPrefixMembers sequences [first, first + kPrefixMembers).
+// The run's first sequence leads; the next ones join in order while the
+// leading block ids they share with the leader, within both contexts' whole
+// blocks, make a prefix of at least min_prefix tokens and the page reads
+// saved, prefix * (members - 1), do not fall: the host planner's rule
+// (prefix_plan.cpp) within the run.  Writes the run's group (first, members,
+// prefix tokens), or first = -1 when it forms none, and the prefix length of
+// each of its sequences (0 outside the group).
+__global__ __launch_bounds__(64) void find_groups_kernel(
+    const int32_t* __restrict__ block_tables, int32_t max_blocks,
+    const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t min_prefix,
+    int32_t* __restrict__ groups, int32_t* __restrict__ seq_prefix_lens) {
+  const int gi = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int first = gi * kPrefixMembers;
+  const int n = min(kPrefixMembers, num_seqs - first);
+  // whole blocks of a context (a length above the table row, a broken
+  // precondition, is cut to the row)
+  auto whole = [&](int s) { return min(max(context_lens[s], 0), max_blocks * kBS) / kBS; };
+  const int floor_min = max(min_prefix, kBS);
+  const int32_t* lead = block_tables + static_cast<int64_t>(first) * max_blocks;
+  int P = whole(first);  // candidate prefix, in blocks
+  int count = 1;
+  for (int m = 1; m < n; ++m) {
+    const int32_t* other = block_tables + static_cast<int64_t>(first + m) * max_blocks;
+    const int limit = min(P, whole(first + m));
+    int common = limit;
+    for (int i0 = 0; i0 < limit; i0 += 64) {  // 64 block ids per step, first mismatch
+      const int i = i0 + lane;
+      const unsigned long long diff = __ballot(i < limit && lead[i] != other[i]);
+      if (diff != 0) {
+        common = i0 + __ffsll(static_cast<long long>(diff)) - 1;
+        break;
+      }
+    }
+    if (common * kBS < floor_min ||
+        static_cast<int64_t>(common) * count < static_cast<int64_t>(P) * (count - 1))
+      break;
+    P = common;
+    ++count;
+  }
+  const bool grouped = count >= 2;  // a member joined: P * kBS >= floor_min
+  if (lane == 0) {
+    groups[3 * gi] = grouped ? first : -1;
+    groups[3 * gi + 1] = grouped ? count : 0;
+    groups[3 * gi + 2] = grouped ? P * kBS : 0;
+  }
+  if (lane < n) seq_prefix_lens[first + lane] = grouped && lane < count ? P * kBS : 0;
+}
+
 // Where a decode call's partitions go: `slots` partial slots per (sequence,
 // head) row; the first pass covers tokens [starts[s], L) (from 0 when starts
 // is null) in up to `parts` partitions written from slot part_base on.
@@ -162,10 +213,104 @@ int dispatch_block(int32_t dtype, int32_t head_dim, int G, void* out, const void
 
 }  // namespace
 
+namespace {
+
+// The prefix pass works in partitions twice as long as the rest's: its
+// workgroups then keep their copy pipeline full for longer (measured 4%
+// faster on 8-sample groups with a 1024-token prefix than equal partitions;
+// four times as long gained nothing more).
+constexpr int kPrefixPartMult = 2;
+
+// Partition of a shared prefix, in tokens, for the rest's partition `part`.
+int32_t prefix_partition(int32_t part) {
+  return static_cast<int32_t>(
+      std::min<int64_t>(static_cast<int64_t>(part) * kPrefixPartMult, 0x40000000));
+}
+
+// Partial slots of a shared-prefix call: the prefix's partitions, then the
+// rest's.
+void shared_slots(int32_t max_context_len, int32_t max_prefix_len, int32_t part, int64_t& pre,
+                  int64_t& rest) {
+  pre = max_prefix_len > 0 ? parts_for(max_prefix_len, prefix_partition(part)) : 0;
+  rest = parts_for(max_context_len, part);
+}
+
+int32_t unsplit_partition(int32_t partition, int32_t max_context_len) {
+  if (partition != 0) return partition;
+  return static_cast<int32_t>(((std::max(max_context_len, 1) + kTile - 1) / kTile) * kTile);
+}
+
+
+// The launches of a call with prefix groups (on the device, at `groups`,
+// num_groups of them): the prefix pass over the groups' shared pages, then
+// pass 1 over each sequence's rest (from seq_prefix_lens[s]) and the merge.
+// pre and rest are the partial slots of the prefix and of the rest.
+int shared_launch(void* out, const void* q, const void* kc, const void* vc, const int32_t* bt,
+                  int32_t mb, const int32_t* lens, int32_t B, int32_t H, int32_t KVH,
+                  int32_t part, int64_t pre, int64_t rest, const int32_t* groups,
+                  int32_t num_groups, const int32_t* seq_prefix_lens, void* ws, float sl2,
+                  hipStream_t st, bool nt) {
+  const int G = H / KVH;
+  const int64_t slots = pre + rest;
+  const int64_t nchunks =  // 32 queries each
+      (static_cast<int64_t>(kPrefixMembers) * G + 31) / 32;
+  const bool split = num_groups > 0 && pre > 0;
+  if (split) {
+    const Partials p = carve(ws, B, H, 128, slots);
+    const int64_t grid = pre * num_groups * nchunks * KVH;
+    auto kernel = nt ? decode_prefix_mfma_kernel<true> : decode_prefix_mfma_kernel<false>;
+    hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(grid)), dim3(64), 0, st,
+                       static_cast<uint16_t*>(out), p, static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(kc), static_cast<const uint16_t*>(vc), bt,
+                       mb, lens, groups, num_groups, B, H, KVH, static_cast<int32_t>(slots),
+                       static_cast<int32_t>(pre), prefix_partition(part), sl2);
+    const int rc = pa_launch_status();
+    if (rc != PA_OK) return rc;
+  }
+  const Split sp{static_cast<int32_t>(slots), static_cast<int32_t>(rest),
+                 {split ? seq_prefix_lens : nullptr, static_cast<int32_t>(pre),
+                  prefix_partition(part)}};
+  return dispatch_group<uint16_t, 128>(G, out, q, kc, vc, bt, mb, lens, B, H, KVH, sp, part,
+                                       sl2, ws, st, nt);
+}
+
+// Workspace of a call that finds its prefix groups (PA_DECODE_FIND_SHARED):
+// the partials of a prefix of up to max_context_len tokens and of the rest,
+// then the groups found (3 int32 per run of kPrefixMembers sequences), then
+// each sequence's prefix length.
+struct FoundLayout {
+  int32_t part, runs;
+  int64_t pre, rest;
+  size_t groups_off, lens_off, total;
+};
+FoundLayout found_layout(int32_t B, int32_t H, int32_t D, int32_t max_context_len,
+                         int32_t partition) {
+  FoundLayout f;
+  f.part = unsplit_partition(partition, max_context_len);
+  shared_slots(max_context_len, max_context_len / kBS * kBS, f.part, f.pre, f.rest);
+  f.runs = (std::max(B, 0) + kPrefixMembers - 1) / kPrefixMembers;
+  f.groups_off = align_up(ws_bytes(B, H, D, f.pre + f.rest));
+  f.lens_off = f.groups_off + align_up(static_cast<size_t>(f.runs) * 3 * sizeof(int32_t));
+  f.total = f.lens_off + static_cast<size_t>(std::max(B, 0)) * sizeof(int32_t);
+  return f;
+}
+
+}  // namespace
+
 extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                             int32_t max_context_len, int32_t partition) {
   if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0) return 0;
   return ws_bytes(num_seqs, num_heads, head_dim, parts_for(max_context_len, partition));
+}
+
+extern "C" size_t pa_decode_workspace_bytes_flags(int32_t num_seqs, int32_t num_heads,
+                                                  int32_t head_dim, int32_t max_context_len,
+                                                  int32_t partition, int32_t flags) {
+  if (!(flags & PA_DECODE_FIND_SHARED))
+    return pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, partition);
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || partition < 0 || max_context_len < 0)
+    return 0;
+  return found_layout(num_seqs, num_heads, head_dim, max_context_len, partition).total;
 }
 
 // pa_decode's checks and launches, on the workspace given.
@@ -177,7 +322,8 @@ static int decode_call(void* out, const void* q, const void* k_cache, const void
                        int32_t max_context_len, void* workspace, size_t workspace_bytes,
                        int32_t dtype, int32_t flags, void* stream) {
   if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
-  if (flags & ~PA_DECODE_STREAM_KV) return PA_ERR_INVALID_ARG;
+  if (flags & ~(PA_DECODE_STREAM_KV | PA_DECODE_FIND_SHARED)) return PA_ERR_INVALID_ARG;
+  const bool find = (flags & PA_DECODE_FIND_SHARED) != 0;
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
       num_blocks <= 0 || partition < 0 || max_context_len < 0)
     return PA_ERR_INVALID_ARG;
@@ -185,6 +331,8 @@ static int decode_call(void* out, const void* q, const void* k_cache, const void
   if ((block_size != 8 && block_size != 16 && block_size != 32 && block_size != 64) ||
       (head_dim != 64 && head_dim != 128))
     return PA_ERR_UNSUPPORTED;
+  if (find && (dtype != PA_BF16 || head_dim != 128 || block_size != kBS))
+    return PA_ERR_UNSUPPORTED;  // the prefix pass runs on the bf16 matrix-core body
   if (partition % kTile != 0) return PA_ERR_INVALID_ARG;
   if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
     return PA_ERR_INVALID_ARG;
@@ -207,11 +355,33 @@ static int decode_call(void* out, const void* q, const void* k_cache, const void
   const int G = num_heads / num_kv_heads;
   const float sl2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool nt = (flags & PA_DECODE_STREAM_KV) != 0;
+  if (find) {
+    if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
+    const FoundLayout f =
+        found_layout(num_seqs, num_heads, head_dim, max_context_len, partition);
+    const int64_t nchunks = (static_cast<int64_t>(kPrefixMembers) * G + 31) / 32;
+    if (f.pre + f.rest > 0x7fffffff || f.rest * num_kv_heads * num_seqs > 0x7fffffffLL ||
+        f.pre * f.runs * nchunks * num_kv_heads > 0x7fffffffLL)
+      return PA_ERR_INVALID_ARG;
+    if (workspace == nullptr || workspace_bytes < f.total) return PA_ERR_WORKSPACE;
+    uint8_t* base = static_cast<uint8_t*>(workspace);
+    int32_t* groups = reinterpret_cast<int32_t*>(base + f.groups_off);
+    int32_t* pre_lens = reinterpret_cast<int32_t*>(base + f.lens_off);
+    hipLaunchKernelGGL(find_groups_kernel, dim3(static_cast<uint32_t>(f.runs)), dim3(64), 0, st,
+                       block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                       static_cast<int32_t>(PA_FIND_SHARED_MIN_PREFIX), groups, pre_lens);
+    const int rc = pa_launch_status();
+    if (rc != PA_OK) return rc;
+    return shared_launch(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                         context_lens, num_seqs, num_heads, num_kv_heads, f.part, f.pre, f.rest,
+                         groups, f.runs, pre_lens, workspace, sl2, st, nt);
+  }
   const Split sp{static_cast<int32_t>(parts), static_cast<int32_t>(parts), {nullptr, 0, part}};
 #define PA_DECODE_BS(BSZ)                                                                      \
   dispatch_block<BSZ>(dtype, head_dim, G, out, q, k_cache, v_cache, block_tables,              \
                       max_blocks_per_seq, context_lens, num_seqs, num_heads, num_kv_heads, sp, \
-                      part, sl2, workspace, st, (flags & PA_DECODE_STREAM_KV) != 0)
+                      part, sl2, workspace, st, nt)
   switch (block_size) {
     case 8: return PA_DECODE_BS(8);
     case 32: return PA_DECODE_BS(32);
@@ -273,8 +443,8 @@ extern "C" int pa_decode_no_alloc(void* out, const void* q, const void* k_cache,
   // The partials pa_decode would need (0 when no sequence can span two
   // partitions) must fit the array: a larger call is refused before any
   // device work.  Invalid arguments are reported by pa_decode's own checks.
-  const size_t need = pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len,
-                                                partition);
+  const size_t need = pa_decode_workspace_bytes_flags(num_seqs, num_heads, head_dim,
+                                                      max_context_len, partition, flags);
   if (need > PA_NO_ALLOC_SCRATCH_BYTES) return PA_ERR_WORKSPACE;
   void* ws = nullptr;
   if (need > 0) {
@@ -287,34 +457,6 @@ extern "C" int pa_decode_no_alloc(void* out, const void* q, const void* k_cache,
                      flags, stream);
 }
 
-namespace {
-
-// The prefix pass works in partitions twice as long as the rest's: its
-// workgroups then keep their copy pipeline full for longer (measured 4%
-// faster on 8-sample groups with a 1024-token prefix than equal partitions;
-// four times as long gained nothing more).
-constexpr int kPrefixPartMult = 2;
-
-// Partition of a shared prefix, in tokens, for the rest's partition `part`.
-int32_t prefix_partition(int32_t part) {
-  return static_cast<int32_t>(
-      std::min<int64_t>(static_cast<int64_t>(part) * kPrefixPartMult, 0x40000000));
-}
-
-// Partial slots of a shared-prefix call: the prefix's partitions, then the
-// rest's.
-void shared_slots(int32_t max_context_len, int32_t max_prefix_len, int32_t part, int64_t& pre,
-                  int64_t& rest) {
-  pre = max_prefix_len > 0 ? parts_for(max_prefix_len, prefix_partition(part)) : 0;
-  rest = parts_for(max_context_len, part);
-}
-
-int32_t unsplit_partition(int32_t partition, int32_t max_context_len) {
-  if (partition != 0) return partition;
-  return static_cast<int32_t>(((std::max(max_context_len, 1) + kTile - 1) / kTile) * kTile);
-}
-
-}  // namespace
 
 extern "C" size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads,
                                                           int32_t head_dim,
@@ -370,25 +512,8 @@ extern "C" int pa_decode_shared_prefix(
   const size_t need = ws_bytes(num_seqs, num_heads, head_dim, slots);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_ERR_WORKSPACE;
   const float sl2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (split) {
-    const Partials p = carve(workspace, num_seqs, num_heads, 128, slots);
-    const int64_t grid = pre * num_groups * nchunks * num_kv_heads;
-    auto kernel = nt ? decode_prefix_mfma_kernel<true> : decode_prefix_mfma_kernel<false>;
-    hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(grid)), dim3(64), 0,
-                       st, static_cast<uint16_t*>(out), p, static_cast<const uint16_t*>(q),
-                       static_cast<const uint16_t*>(k_cache),
-                       static_cast<const uint16_t*>(v_cache), block_tables, max_blocks_per_seq,
-                       context_lens, prefix_groups, num_groups, num_seqs, num_heads, num_kv_heads,
-                       static_cast<int32_t>(slots), static_cast<int32_t>(pre),
-                       prefix_partition(part), sl2);
-    const int rc = pa_launch_status();
-    if (rc != PA_OK) return rc;
-  }
-  const Split sp{static_cast<int32_t>(slots), static_cast<int32_t>(rest),
-                 {split ? seq_prefix_lens : nullptr, static_cast<int32_t>(pre),
-                  prefix_partition(part)}};
-  return dispatch_group<uint16_t, 128>(G, out, q, k_cache, v_cache, block_tables,
-                                       max_blocks_per_seq, context_lens, num_seqs, num_heads,
-                                       num_kv_heads, sp, part, sl2, workspace, st, nt);
+  return shared_launch(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, num_heads, num_kv_heads, part, pre, rest, prefix_groups,
+                       split ? num_groups : 0, seq_prefix_lens, workspace, sl2,
+                       static_cast<hipStream_t>(stream), nt);
 }

@@ -13,7 +13,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from ._lib import PA_BF16, PA_DECODE_STREAM_KV, PA_F32, check, lib
+from ._lib import PA_BF16, PA_DECODE_FIND_SHARED, PA_DECODE_STREAM_KV, PA_F32, check, lib
 
 BLOCK_SIZE = 16
 _DT = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
@@ -39,8 +39,8 @@ def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def _flags(stream_kv: bool) -> int:
-    return PA_DECODE_STREAM_KV if stream_kv else 0
+def _flags(stream_kv: bool, find_shared: bool = False) -> int:
+    return (PA_DECODE_STREAM_KV if stream_kv else 0) | (PA_DECODE_FIND_SHARED if find_shared else 0)
 
 
 def _dtype(t: torch.Tensor) -> int:
@@ -131,21 +131,28 @@ def pa_copy_blocks(k_cache, v_cache, pairs):
         _dtype(k_cache), _stream(k_cache)))
 
 
-def pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, partition) -> int:
-    return int(lib().pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len,
-                                               partition))
+def pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, partition,
+                              find_shared: bool = False) -> int:
+    """Workspace of pa_decode; ``find_shared``: with PA_DECODE_FIND_SHARED."""
+    return int(lib().pa_decode_workspace_bytes_flags(num_seqs, num_heads, head_dim,
+                                                     max_context_len, partition,
+                                                     _flags(False, find_shared)))
 
 
-def decode_workspace(num_seqs, num_heads, head_dim, max_context_len, partition, device="cuda"):
-    n = pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, partition)
+def decode_workspace(num_seqs, num_heads, head_dim, max_context_len, partition, device="cuda",
+                     find_shared: bool = False):
+    n = pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, partition,
+                                  find_shared)
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float, partition: int,
               max_context_len: int, workspace=None, check_device_args=False,
-              stream_kv: bool = False):
+              stream_kv: bool = False, find_shared: bool = False):
     """``stream_kv``: PA_DECODE_STREAM_KV, for calls in which no block is read
-    by two sequences (see include/pa.h)."""
+    by two sequences; ``find_shared``: PA_DECODE_FIND_SHARED, the call finds
+    prefix groups itself and reads their shared pages once (see
+    include/pa.h)."""
     nb, kvh, d, bs = _cache_dims(k_cache, v_cache)
     dev = k_cache.device
     _arg(dev, "out", out)
@@ -168,7 +175,7 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float
         _check_tables(block_tables, context_lens, nb, bs)
         if int(context_lens.max()) > max_context_len:
             raise ValueError("max_context_len below a context length")
-    need = pa_decode_workspace_bytes(B, H, d, max_context_len, partition)
+    need = pa_decode_workspace_bytes(B, H, d, max_context_len, partition, find_shared)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     wptr = workspace.data_ptr() if workspace is not None else None
@@ -177,11 +184,12 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float
         out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
         block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(), B, H, kvh, d, bs,
         nb, float(scale), int(partition), int(max_context_len), wptr, wbytes, _dtype(q),
-        _flags(stream_kv), _stream(q)))
+        _flags(stream_kv, find_shared), _stream(q)))
 
 
 def pa_decode_no_alloc(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
-                       partition: int, max_context_len: int, stream_kv: bool = False):
+                       partition: int, max_context_len: int, stream_kv: bool = False,
+                       find_shared: bool = False):
     """pa_decode with the partials in the library's own device array: no
     workspace, no allocation (see include/pa.h for the size limit and the rule
     that overlapping calls on one GPU race)."""
@@ -201,8 +209,8 @@ def pa_decode_no_alloc(out, q, k_cache, v_cache, block_tables, context_lens, sca
     check("pa_decode_no_alloc", lib().pa_decode_no_alloc(
         out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
         block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(), B, H, kvh, d, bs,
-        nb, float(scale), int(partition), int(max_context_len), _dtype(q), _flags(stream_kv),
-        _stream(q)))
+        nb, float(scale), int(partition), int(max_context_len), _dtype(q),
+        _flags(stream_kv, find_shared), _stream(q)))
 
 
 def pa_prefix_plan(block_tables, context_lens, max_members: int = 8, min_prefix: int = 256,

@@ -49,11 +49,13 @@ def assert_pool_equal(w: DeviceWorkload, st) -> None:
     assert np.array_equal(raw_bits(gv), raw_bits(st.v_cache)), "v_cache differs from the oracle"
 
 
-def gpu_step(script, partition=None, scale=None, step=0, workload=None, shared_prefix=None):
+def gpu_step(script, partition=None, scale=None, step=0, workload=None, shared_prefix=None,
+             find_shared=False):
     """Run the script's setup and step on the GPU; return (workload, out,
     host tables, host lens).  ``shared_prefix`` = (max_members, min_prefix)
     runs decode through pa_decode_shared_prefix with the groups
-    pa_prefix_plan finds (kept in ``w.prefix_plan``)."""
+    pa_prefix_plan finds (kept in ``w.prefix_plan``); ``find_shared`` runs it
+    through pa_decode with PA_DECODE_FIND_SHARED."""
     w = workload or DeviceWorkload(script)
     w.run_step()
     bt, lens, bt_h, lens_h = w.batch_tables()
@@ -65,7 +67,7 @@ def gpu_step(script, partition=None, scale=None, step=0, workload=None, shared_p
         part = s.partition if partition is None else partition
         if shared_prefix is None:
             pa_decode(out, q, w.k_cache, w.v_cache, bt, lens, sc, part, int(max(lens_h.max(), 0)),
-                      check_device_args=True)
+                      check_device_args=True, find_shared=find_shared)
         else:
             groups, pre, mp = pa_prefix_plan(bt_h, lens_h, *shared_prefix)
             w.prefix_plan = (groups, pre, mp)

@@ -1,6 +1,8 @@
 """CPU checks of bench.py's command line and helpers (no GPU)."""
 
 import csv
+
+import numpy as np
 import os
 import subprocess
 import sys
@@ -87,3 +89,23 @@ def test_counter_summary_derives_clock_busy_share_and_bytes(tmp_path):
     assert abs(at["@prefill_chunk_pp_kernel_mfma_busy_frac"] - 0.25) < 1e-9
     assert at["@prefill_chunk_pp_kernel_hbm_bytes"] == 1000 * 1024 * 2 + 10 * 1024
     assert "@sources_sha256: " + bench.sources_sha256(bench.PREFILL_SOURCES) in text
+
+
+def test_found_groups_follow_the_host_planner_on_each_run():
+    from paged_kv_cache_219_amd.kernels import pa_prefix_plan
+    from tests.test_gpu_shared_prefix import LAYOUT, _batch
+    g = np.random.default_rng(5)
+    for shift in range(9):
+        layout = [(1, 0, [3])] * shift + LAYOUT + [(6, 512, [1, 2, 3, 4, 5, 6])]
+        bt, lens, _ = _batch(g, layout, 600)
+        groups, pre = bench.found_groups(bt, lens)
+        want_pre = np.zeros(len(lens), np.int32)
+        want = []
+        for first in range(0, len(lens), 8):
+            gp, _, _ = pa_prefix_plan(bt[first:first + 8], lens[first:first + 8], 8, 256)
+            if len(gp) and gp[0][0] == 0:
+                n, p = int(gp[0][1]), int(gp[0][2])
+                want.append((first, n, p))
+                want_pre[first:first + n] = p
+        assert groups == want, shift
+        assert np.array_equal(pre, want_pre), shift

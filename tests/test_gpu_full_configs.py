@@ -49,14 +49,17 @@ def whole_reference(sc, st):
 
 
 @pytest.mark.parametrize("name", ["decode_bf16", "gqa_decode_bf16", "shared_prefix_bf16",
-                                  "shared_prefix_bf16:grouped", "chunked_prefill_bf16"])
+                                  "shared_prefix_bf16:grouped", "shared_prefix_bf16:found",
+                                  "chunked_prefill_bf16"])
 def test_full_size_whole_tensor(name):
     say(f"full-size {name}: GPU step")
     name, _, mode = name.partition(":")
     sc = memoize_draws(config_script(name))
-    # grouped: through pa_decode_shared_prefix with the planner's default groups
-    w, out, bt_h, lens_h = gpu_step(sc, shared_prefix=(8, 256) if mode else None)
-    if mode:
+    # grouped: through pa_decode_shared_prefix with the planner's default groups;
+    # found: through pa_decode finding the groups on the device
+    w, out, bt_h, lens_h = gpu_step(sc, shared_prefix=(8, 256) if mode == "grouped" else None,
+                                    find_shared=mode == "found")
+    if mode == "grouped":
         assert len(w.prefix_plan[0]) == len(sc.batch) // 8
     say("  oracle build (whole script)")
     st = run.build(sc)

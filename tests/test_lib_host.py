@@ -16,6 +16,7 @@ import pytest
 
 from oracle.alloc_model import AllocModel
 from paged_kv_cache_219_amd import BlockAllocator, header_functions, lib
+from paged_kv_cache_219_amd import _lib
 from paged_kv_cache_219_amd._lib import PA_BF16, PA_F32
 
 
@@ -25,7 +26,7 @@ def test_library_exports_every_declared_function():
     L = lib()
     missing = [n for n in names if not hasattr(L, n)]
     assert not missing, missing
-    assert L.pa_version() == 2
+    assert L.pa_version() == _lib.ABI_VERSION == 3
     for code in range(-7, 1):
         assert L.pa_status_str(code).decode().startswith("PA_")
 
@@ -51,7 +52,17 @@ def test_host_argument_checks_reject_before_launch():
                            a["D"], a["BS"], a["NB"], 0.1, a["part"], a["maxL"], None, 0,
                            a.get("dt", PA_BF16), a.get("flags", 0), None)
     assert dec() == -1
-    assert dec(H=8, flags=2) == -1          # reserved flag bit
+    assert dec(H=8, flags=4) == -1          # reserved flag bit
+    # finding shared prefixes: bf16, head_dim 128, 16-token blocks, and its own workspace size
+    assert dec(H=8, flags=2) == -6
+    assert dec(H=8, flags=3, D=64) == -5
+    assert dec(H=8, flags=2, dt=PA_F32) == -5
+    assert dec(H=8, flags=2, BS=32) == -5
+    L.pa_decode_workspace_bytes_flags.restype = ctypes.c_size_t
+    assert L.pa_decode_workspace_bytes_flags(2, 8, 128, 100, 64, 0) == \
+        L.pa_decode_workspace_bytes(2, 8, 128, 100, 64)
+    found = L.pa_decode_workspace_bytes_flags(9, 8, 128, 1000, 64, 2)
+    assert found >= L.pa_decode_shared_prefix_workspace_bytes(9, 8, 128, 1000, 992, 64) + 9 * 4 + 2 * 12
     assert dec(H=8, part=100) == -1
     assert dec(H=8, part=64) == -6
     assert dec(H=8, maxL=8 * 16 + 1) == -1
