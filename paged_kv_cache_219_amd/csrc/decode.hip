@@ -99,29 +99,55 @@ __global__ __launch_bounds__(64) void find_groups_kernel(
     const int32_t* __restrict__ block_tables, int32_t max_blocks,
     const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t min_prefix,
     int32_t* __restrict__ groups, int32_t* __restrict__ seq_prefix_lens) {
+  static_assert(kPrefixMembers == 8, "8 lanes per member, 8 members per wave");
   const int gi = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int first = gi * kPrefixMembers;
   const int n = min(kPrefixMembers, num_seqs - first);
-  // whole blocks of a context (a length above the table row, a broken
-  // precondition, is cut to the row)
-  auto whole = [&](int s) { return min(max(context_lens[s], 0), max_blocks * kBS) / kBS; };
-  const int floor_min = max(min_prefix, kBS);
+  // whole blocks of each member's context (lane m holds member m's; a length
+  // above the table row, a broken precondition, is cut to the row)
+  const int my_whole = lane < n ? min(max(context_lens[first + lane], 0), max_blocks * kBS) / kBS : 0;
+  const int whole0 = __builtin_amdgcn_readfirstlane(my_whole);
+  // Leading block ids each member m >= 1 shares with the leader, all members
+  // at once: lane 8 m + j compares positions j, j + 8, ... of member m's row
+  // with the leader's, eight positions per pass (one round of loads).
+  const int m = lane >> 3, j = lane & 7;
+  const int whole_m = __shfl(my_whole, m, 64);  // every lane takes part in the exchange
+  const int limit = m >= 1 && m < n ? min(whole0, whole_m) : 0;
   const int32_t* lead = block_tables + static_cast<int64_t>(first) * max_blocks;
-  int P = whole(first);  // candidate prefix, in blocks
-  int count = 1;
-  for (int m = 1; m < n; ++m) {
-    const int32_t* other = block_tables + static_cast<int64_t>(first + m) * max_blocks;
-    const int limit = min(P, whole(first + m));
-    int common = limit;
-    for (int i0 = 0; i0 < limit; i0 += 64) {  // 64 block ids per step, first mismatch
-      const int i = i0 + lane;
-      const unsigned long long diff = __ballot(i < limit && lead[i] != other[i]);
-      if (diff != 0) {
-        common = i0 + __ffsll(static_cast<long long>(diff)) - 1;
-        break;
-      }
+  const int32_t* other = block_tables + static_cast<int64_t>(first + (m < n ? m : 0)) * max_blocks;
+  int mine = limit;  // this lane's first mismatch (or the limit)
+  for (int base = 0; __any(base < limit && mine == limit); base += 64) {
+    int a[8], b[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int pos = base + j + 8 * k;
+      a[k] = pos < limit ? lead[pos] : 0;
+      b[k] = pos < limit ? other[pos] : 0;
     }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int pos = base + j + 8 * k;
+      if (mine == limit && pos < limit && a[k] != b[k]) mine = pos;
+    }
+    // the member's eight lanes have now compared every position below
+    // base + 64: a mismatch among them is the member's first one
+    int lo = mine;
+    lo = min(lo, __shfl_xor(lo, 1, 64));
+    lo = min(lo, __shfl_xor(lo, 2, 64));
+    lo = min(lo, __shfl_xor(lo, 4, 64));
+    if (lo < base + 64) mine = lo;  // every position below lo was compared equal
+  }
+  int lcp = mine;  // member m's common prefix with the leader, in blocks
+  lcp = min(lcp, __shfl_xor(lcp, 1, 64));
+  lcp = min(lcp, __shfl_xor(lcp, 2, 64));
+  lcp = min(lcp, __shfl_xor(lcp, 4, 64));
+  // the host planner's greedy rule, on the members' common prefixes in order
+  const int floor_min = max(min_prefix, kBS);
+  int P = whole0;  // candidate prefix, in blocks
+  int count = 1;
+  for (int mm = 1; mm < n; ++mm) {
+    const int common = min(__shfl(lcp, 8 * mm, 64), P);
     if (common * kBS < floor_min ||
         static_cast<int64_t>(common) * count < static_cast<int64_t>(P) * (count - 1))
       break;
