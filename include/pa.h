@@ -335,6 +335,8 @@ int pa_decode_shared_prefix(void* out, const void* q, const void* k_cache, const
  *   query_start_loc  device int32 [num_seqs + 1], non-decreasing, [0] = 0.
  *   max_query_len    host upper bound of n_q (sizes the grid).
  * bf16 only (matrix-core path); PA_F32 returns PA_ERR_UNSUPPORTED.
+ * num_kv_heads above 2^19 (a cache block of more than 2^31 bytes) returns
+ * PA_ERR_INVALID_ARG.
  */
 int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -48,6 +48,7 @@ extern "C" int pa_prefill_chunk(void* out, const void* q, const void* k_cache,
       max_blocks_per_seq <= 0 || num_blocks <= 0)
     return PA_ERR_INVALID_ARG;
   if (num_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (num_kv_heads > (1 << 19)) return PA_ERR_INVALID_ARG;  // a cache block's bytes fit 31 bits
   if (dtype != PA_BF16 || head_dim != kD || block_size != kBS) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0 || max_query_len == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start_loc || !context_lens)

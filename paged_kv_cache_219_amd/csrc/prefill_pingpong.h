@@ -76,8 +76,15 @@ __device__ __forceinline__ void pp_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Wait until at most n of this wave's vector-memory loads are outstanding
-// (n even: whole steps of two copies each; up to 2 (kRingPP - 3)).
+// Wait until at most N of this wave's vector-memory loads are outstanding.
+template <int N>
+__device__ __forceinline__ void pp_wait_loads() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// The same for a count known only at run time (n even: whole steps of two
+// copies each; up to 2 (kRingPP - 3)): a chain of compares and branches, so
+// the loop's steady state uses pp_wait_loads instead.
 __device__ __forceinline__ void pp_wait_copies(int n) {
   if (n >= 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
   else if (n >= 10) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
@@ -152,11 +159,12 @@ __device__ __forceinline__ void prefill_tile_pp(
     for (int kk = 0; kk < 8; ++kk) qreg[kk] = *reinterpret_cast<const uint4*>(qrow + 16 * kk);
   }
 
-  // The block id of this wave's page of a step: a scalar load, issued a phase
-  // before the copy that needs it (its wait, which also waits for outstanding
-  // LDS reads, then costs nothing).  Pages past the last needed token name
-  // logical block 0 (always valid): their scores are masked and their values
-  // weighted by 0.
+  // The block id of this wave's page of a step: a scalar load issued at the
+  // start of the softmax phase before the one whose copy needs it, and taken
+  // after that phase's operand wait (a wait for it at its use would also wait
+  // for the operand reads of the matrix phase in between).  Pages past the
+  // last needed token name logical block 0 (always valid): their scores are
+  // masked and their values weighted by 0.
   const int32_t* bt_row = block_tables + static_cast<int64_t>(s) * max_blocks;
   const int pw = pa::ring::page_of<kWavesPP>(wave);
   auto block_of = [&](int st) {
@@ -171,16 +179,18 @@ __device__ __forceinline__ void prefill_tile_pp(
     asm volatile("" : "+v"(qreg[kk].x), "+v"(qreg[kk].y), "+v"(qreg[kk].z), "+v"(qreg[kk].w));
 
   const RingLane<kWavesPP> rl(wave, lane);
-  const int64_t page_bytes = static_cast<int64_t>(kPageElems) * 2;
-  const int64_t blk_bytes = static_cast<int64_t>(num_kv_heads) * page_bytes;
+  // a block's bytes fit 32 bits (the entry point bounds num_kv_heads), so a
+  // copy's source offset is one 32 x 32 -> 64-bit product
+  const uint32_t page_bytes = static_cast<uint32_t>(kPageElems) * 2;
+  const uint32_t blk_bytes = static_cast<uint32_t>(num_kv_heads) * page_bytes;
   const int64_t head_bytes = static_cast<int64_t>(g) * page_bytes;
   const uint32_t u0 = 64u * static_cast<uint32_t>(wave);  // this wave's run of the step
   const uint32_t ring_lds = pa::ring::lds_addr(&ring[0]);
   const char* lds = reinterpret_cast<const char*>(&ring[0]);
-  const char* kc_b = reinterpret_cast<const char*>(kc);
-  const char* vc_b = reinterpret_cast<const char*>(vc);
+  const char* kc_b = reinterpret_cast<const char*>(kc) + head_bytes;
+  const char* vc_b = reinterpret_cast<const char*>(vc) + head_bytes;
   auto issue = [&](int st, int phys) {
-    const int64_t src = static_cast<int64_t>(phys) * blk_bytes + head_bytes;
+    const uint64_t src = static_cast<uint64_t>(static_cast<uint32_t>(phys)) * blk_bytes;
     const uint32_t dst = ring_lds + static_cast<uint32_t>(st % kRingPP) * kStepBytes + u0 * 16;
     dma16_sbase(kc_b + src, rl.k_src[0], dst);
     dma16_sbase(vc_b + src, rl.v_src[0], dst + kVBytes);
@@ -248,7 +258,8 @@ __device__ __forceinline__ void prefill_tile_pp(
     __builtin_amdgcn_s_setprio(0);
     // this wave's copy of step j + 2 has landed (later steps may stay in
     // flight; the softmax phases issue the copies)
-    pp_wait_copies(2 * max(0, min(nsteps - 1, j + kRingPP - 2) - (j + 2)));
+    if (j + kRingPP - 2 <= nsteps - 1) pp_wait_loads<2 * (kRingPP - 4)>();
+    else pp_wait_copies(2 * max(0, nsteps - 1 - (j + 2)));
   };
 
   // ---- softmax phase of step j: the copy of step j + kRingPP - 1 (it
@@ -259,6 +270,7 @@ __device__ __forceinline__ void prefill_tile_pp(
   auto softmax_phase = [&](int j) {
     const int t0 = j * kStep;
     if (j + kRingPP - 1 < nsteps) issue(j + kRingPP - 1, next_phys);
+    if (j + kRingPP < nsteps) next_phys = block_of(j + kRingPP);
     float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] = sa[i];
@@ -284,7 +296,9 @@ __device__ __forceinline__ void prefill_tile_pp(
     // the operands read in matrix phase j have landed
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     operands_ready();
-    if (j + kRingPP < nsteps) next_phys = block_of(j + kRingPP);
+    // the block id has landed too: taken here, the next softmax phase's copy
+    // needs no wait (which would also drain the matrix phase's operand reads)
+    asm volatile("" : "+s"(next_phys));
     if (tail) {  // values of tokens at or past L may be anything: 0 * NaN
 #pragma unroll
       for (int pg = 0; pg < kPages; ++pg) {

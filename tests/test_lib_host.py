@@ -74,6 +74,9 @@ def test_host_argument_checks_reject_before_launch():
     # prefill: fp32 is not supported (matrix-core path is bf16)
     assert L.pa_prefill_chunk(fake, fake, fake, fake, fake, 8, fake, fake, 2, 16, 8, 8, 128, 16, 64,
                               0.1, PA_F32, None) == -5
+    # a cache block must fit 31 bits: num_kv_heads <= 2^19
+    assert L.pa_prefill_chunk(fake, fake, fake, fake, fake, 8, fake, fake, 2, 16, 1 << 20, 1 << 20,
+                              128, 16, 64, 0.1, PA_BF16, None) == -1
 
 
 def _state(c: BlockAllocator, m: AllocModel):
