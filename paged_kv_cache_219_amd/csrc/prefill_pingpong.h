@@ -149,6 +149,7 @@ __device__ __forceinline__ void prefill_tile_pp(
   const int my_row = min(wg_row0 + wave + 8 * qn, n_q - 1);
   const int my_pos = first_pos + my_row;
   const int wave_first = first_pos + wg_row0 + wave;  // lowest position among the wave's rows
+  const int j_edge = (wave_first + 1) / kStep;        // first step with 32 j + 31 > wave_first
 
   // Q^T operand: lane (qn, hh) holds dims 16 kk + 8 hh .. + 7 of its row.
   uint4 qreg[8];
@@ -274,8 +275,10 @@ __device__ __forceinline__ void prefill_tile_pp(
     float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] = sa[i];
-    const bool tail = t0 + kStep > L;
-    if (t0 + kStep - 1 > wave_first || tail) {  // diagonal or tail step
+    // a diagonal or tail step: 32 j + 31 > wave_first (a tail step, 32 j + 32
+    // > L > wave_first, is one), i.e. j >= j_edge -- one scalar compare
+    const bool edge = j >= j_edge;
+    if (edge) {
       const int lim = min(my_pos, L - 1) - t0 - 8 * hh;  // keep offsets <= lim
 #pragma unroll
       for (int i = 0; i < 16; ++i)
@@ -299,7 +302,7 @@ __device__ __forceinline__ void prefill_tile_pp(
     // the block id has landed too: taken here, the next softmax phase's copy
     // needs no wait (which would also drain the matrix phase's operand reads)
     asm volatile("" : "+s"(next_phys));
-    if (tail) {  // values of tokens at or past L may be anything: 0 * NaN
+    if (edge && t0 + kStep > L) {  // values of tokens at or past L may be anything: 0 * NaN
 #pragma unroll
       for (int pg = 0; pg < kPages; ++pg) {
         const int keep = L - (t0 + 16 * pg + 8 * hh);
