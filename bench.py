@@ -119,10 +119,13 @@ def unique_kv_bytes(tables, lens, spec) -> int:
 
 
 def bench_decode(name: str, steps: int, warmup: int, mode: str = ""):
-    """One decode workload through pa_decode.  ``mode`` "grouped": through
-    pa_decode_shared_prefix with prefix groups planned on the host every step
-    (pa_prefix_plan over that step's block tables); "found": through
-    pa_decode with PA_DECODE_FIND_SHARED (the call finds the groups)."""
+    """One decode workload.  Each step: the allocator maps one new token per
+    sequence on the host, the step's tables go to the device, copy-on-write
+    copies run, pa_reshape_and_cache writes the new tokens, and pa_decode
+    attends; ``mode`` "grouped": pa_decode_shared_prefix instead, with prefix
+    groups planned on the host every step (pa_prefix_plan over that step's
+    block tables); "found": pa_decode with PA_DECODE_FIND_SHARED (the call
+    finds the groups)."""
     grouped = mode == "grouped"
     found = mode == "found"
     import torch
@@ -171,8 +174,11 @@ def bench_decode(name: str, steps: int, warmup: int, mode: str = ""):
     seqs = np.array(sc.batch, np.int64)
     ones = np.ones(B, np.int32)
     # The step's host-made arrays (slots, tables, lengths, copy-on-write pairs,
-    # prefix groups) share one pinned buffer per ring slot and go to the device
-    # in one copy.
+    # prefix groups) share one pinned buffer per ring slot and go to the
+    # device in one copy, into that slot's device buffer, on a stream of their
+    # own: the copy of step i runs as soon as the host has made its arrays
+    # (the host runs ahead of the GPU), and the compute stream only waits for
+    # its event, instead of for a copy ordered behind the previous step.
     fields = [("slots", torch.int64, (B,)), ("tab", torch.int32, (B, mb)),
               ("len", torch.int32, (B,)), ("cow", torch.int32, (B, 2)),
               ("grp", torch.int32, (B, 3)), ("pre", torch.int32, (B,))]
@@ -184,18 +190,28 @@ def bench_decode(name: str, steps: int, warmup: int, mode: str = ""):
     def carve(buf):
         return {f: buf[offs[f]:offs[f] + int(np.prod(shape)) * torch.tensor([], dtype=dt).element_size()]
                 .view(dt).view(*shape) for f, dt, shape in fields}
-    R = 3  # ring of pinned host buffers
-    pin = []
+    # Ring of R slots, each a pinned host buffer, a device buffer and the
+    # event of its copy.  A slot is free again once the step that used it has
+    # finished; the compute stream records that every RING_EVERY steps (every
+    # event in the stream costs the GPU a few microseconds), and the host
+    # waits, before it reuses a slot, for the first such event at or after
+    # the slot's last step.
+    RING_EVERY = 4
+    R = 2 * RING_EVERY
+    ring = []
     for _ in range(R):
         hb = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
-        pin.append((hb, carve(hb), torch.cuda.Event()))
-    d_buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    d = carve(d_buf)
-    d_slots, d_tab, d_len, d_cow = d["slots"], d["tab"], d["len"], d["cow"]
-    d_grp, d_pre = d["grp"], d["pre"]
+        db = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        ring.append((hb, carve(hb), db, carve(db), torch.cuda.Event()))
+    done = {}  # step -> event recorded after that step's kernels
     stream = torch.cuda.current_stream(dev)
+    copy_stream = torch.cuda.Stream(dev)
+    # Events around the decode call on the warmup steps only (a pair of
+    # events costs the step several microseconds), past the first two (the
+    # first launches also load code).
+    ev_from = 2 if warmup > 2 else 0
     dec_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
+              for _ in range(warmup)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     kv_total = 0
@@ -208,8 +224,14 @@ def bench_decode(name: str, steps: int, warmup: int, mode: str = ""):
             torch.cuda.synchronize()
             wall0 = time.perf_counter()
             t0.record(stream)
-        hb, h, ev = pin[i % R]
-        ev.synchronize()  # the copy that last read this ring slot is done
+        hb, h, d_buf, d, copied = ring[i % R]
+        if i >= R:  # the slot's last step, i - R, is done
+            j = (i - R) | (RING_EVERY - 1)  # the first event at or after it (a power of two)
+            done[j].synchronize()
+            for old in [k for k in done if k < j]:
+                del done[old]
+        d_slots, d_tab, d_len, d_cow = d["slots"], d["tab"], d["len"], d["cow"]
+        d_grp, d_pre = d["grp"], d["pre"]
         _, cow, tables, lens = w.alloc.batch_append(
             seqs, ones, mb, tables_out=h["tab"].numpy(), lens_out=h["len"].numpy(),
             slots_out=h["slots"].numpy(), cow_out=h["cow"].numpy())
@@ -221,8 +243,10 @@ def bench_decode(name: str, steps: int, warmup: int, mode: str = ""):
             plan_groups = ng
         # prefix groups only when grouped, copy-on-write pairs only when present
         n_copy = nbytes if grouped else (offs["grp"] if len(cow) else offs["cow"])
-        d_buf[:n_copy].copy_(hb[:n_copy], non_blocking=True)
-        ev.record(stream)
+        with torch.cuda.stream(copy_stream):
+            d_buf[:n_copy].copy_(hb[:n_copy], non_blocking=True)
+        copied.record(copy_stream)
+        stream.wait_event(copied)
         if len(cow):
             pa_copy_blocks(w.k_cache, w.v_cache, d_cow[: len(cow)])
         pa_reshape_and_cache(ks[i], vs[i], w.k_cache, w.v_cache, d_slots)
@@ -234,8 +258,8 @@ def bench_decode(name: str, steps: int, warmup: int, mode: str = ""):
         else:
             once = blocks_read_once(tables)
         timed = i >= warmup
-        if timed:
-            dec_ev[i - warmup][0].record(stream)
+        if ev_from <= i < warmup:
+            dec_ev[i][0].record(stream)
         if grouped:
             pa_decode_shared_prefix(out, qs[i], w.k_cache, w.v_cache, d_tab, d_len, spec.scale,
                                     spec.partition, int(lens.max()), d_grp[:ng], d_pre, max_pre,
@@ -244,15 +268,20 @@ def bench_decode(name: str, steps: int, warmup: int, mode: str = ""):
             pa_decode(out, qs[i], w.k_cache, w.v_cache, d_tab, d_len, spec.scale, spec.partition,
                       int(lens.max()), ws, stream_kv=once, find_shared=found)
         streamed += once
+        if ev_from <= i < warmup:
+            dec_ev[i][1].record(stream)
+        if i % RING_EVERY == RING_EVERY - 1:
+            done[i] = torch.cuda.Event()
+            done[i].record(stream)
         if timed:
-            dec_ev[i - warmup][1].record(stream)
             kv_total += kv_bytes(lens, spec)
             ncow_total += len(cow)
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     step_ms = t0.elapsed_time(t1) / steps
-    in_step_ms = float(np.mean([a.elapsed_time(b) for a, b in dec_ev]))
+    in_step_ms = (float(np.mean([a.elapsed_time(b) for a, b in dec_ev[ev_from:]]))
+                  if warmup > ev_from else None)
     kv_step = kv_total / steps
 
     # The kernel alone: the last step's call again, timed launch by launch with
@@ -285,7 +314,7 @@ def bench_decode(name: str, steps: int, warmup: int, mode: str = ""):
         # scrubbed launches of the last step's call: median (the figure), min, p90, mean
         "decode_ms": dec_ms, "decode_ms_min": float(dec_t.min()),
         "decode_ms_p90": float(np.percentile(dec_t, 90)), "decode_ms_mean": float(dec_t.mean()),
-        "decode_ms_in_step": in_step_ms,  # inside the step loop, mean
+        "decode_ms_in_step": in_step_ms,  # inside the step loop (warmup steps), mean
         "launch_kv_bytes": kv_last,        # logical: every sequence's pages
         "launch_unique_kv_bytes": uniq_last,  # each distinct page counted once
         # HBM rate on the bytes the method must move (a shared page once)
@@ -355,7 +384,10 @@ def bench_prefill(name: str, steps: int, warmup: int):
     v = to_device(np.concatenate([a[1] for a in kv]), spec.dtype, dev)
     d_slots = torch.from_numpy(np.concatenate([np.asarray(s, np.int64) for s in slots])).to(dev)
     stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    # events around the prefill call on the warmup steps only (a pair of
+    # events costs the step several microseconds), past the first two
+    ev_from = 2 if warmup > 2 else 0
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(warmup)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     max_q = max(sc.query_lens)
@@ -364,15 +396,16 @@ def bench_prefill(name: str, steps: int, warmup: int):
             torch.cuda.synchronize()
             t0.record(stream)
         pa_reshape_and_cache(k, v, w.k_cache, w.v_cache, d_slots)
-        if i >= warmup:
-            ev[i - warmup][0].record(stream)
+        if ev_from <= i < warmup:
+            ev[i][0].record(stream)
         pa_prefill_chunk(out, q, w.k_cache, w.v_cache, bt, qsl, lens, max_q, spec.scale)
-        if i >= warmup:
-            ev[i - warmup][1].record(stream)
+        if ev_from <= i < warmup:
+            ev[i][1].record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
     step_ms = t0.elapsed_time(t1) / steps
-    in_step_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    in_step_ms = (float(np.mean([a.elapsed_time(b) for a, b in ev[ev_from:]]))
+                  if warmup > ev_from else None)
     # the kernel alone, scrubbed launches; the median is the figure reported
     pf_t = scrubbed_launch_times(
         lambda: pa_prefill_chunk(out, q, w.k_cache, w.v_cache, bt, qsl, lens, max_q, spec.scale),
@@ -387,7 +420,7 @@ def bench_prefill(name: str, steps: int, warmup: int):
         # scrubbed launches: median (the figure), min, p90, mean
         "prefill_ms": pf_ms, "prefill_ms_min": float(pf_t.min()),
         "prefill_ms_p90": float(np.percentile(pf_t, 90)), "prefill_ms_mean": float(pf_t.mean()),
-        "prefill_ms_in_step": in_step_ms,  # right after the chunk's cache write, mean
+        "prefill_ms_in_step": in_step_ms,  # right after the chunk's cache write (warmup steps), mean
         "flops_per_call": flops,
         "prefill_TFLOPs": flops / (pf_ms * 1e-3) / 1e12,
         "query_tokens_per_s": sum(sc.query_lens) / (step_ms * 1e-3),
@@ -1093,8 +1126,9 @@ def main():
         else:
             extra = (f" (effective {r['decode_effective_GBs']:.0f} GB/s)"
                      if r["launch_kv_bytes"] != r["launch_unique_kv_bytes"] else "")
-            print(f"[bench] {name}: decode {r['decode_ms']:.3f} ms = {r['decode_kv_GBs']:.0f} GB/s"
-                  f" of unique KV{extra}", file=sys.stderr, flush=True)
+            print(f"[bench] {name}: step {r['ms_per_step']:.3f} ms, decode {r['decode_ms']:.3f} ms"
+                  f" = {r['decode_kv_GBs']:.0f} GB/s of unique KV{extra}", file=sys.stderr,
+                  flush=True)
         extras.append(r)
     copy = None if a.no_copy_calibration else copy_calibration()
     if copy:

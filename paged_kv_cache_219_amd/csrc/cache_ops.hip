@@ -18,13 +18,15 @@ namespace {
 // One 256-thread workgroup per (group of X consecutive tokens, kv head),
 // X = 16 / element size: the number of tokens in one 16-byte unit of the
 // d-major value page.  Waves 0-1 write the keys, waves 2-3 the values, so the
-// two halves' loads and stores are in flight together.
+// two halves' loads and stores are in flight together.  Each thread issues its
+// data loads before it needs a slot (only the stores' addresses depend on the
+// slots), so the slot and data loads wait out one memory latency together.
 //  * keys: the X tokens' rows as 16-byte chunks, each to its x-packed place;
-//  * values: when the group's slots are X consecutive slots starting at a
-//    multiple of X (the common case when a chunk of a sequence is written),
-//    each thread gathers one dimension of the X tokens and stores it as one
-//    16-byte unit of the page; otherwise (scattered tokens, e.g. one new
-//    token per sequence) each thread stores its dimension of every token.
+//  * values: each thread holds one dimension of the X tokens; when the group's
+//    slots are X consecutive slots starting at a multiple of X (the common
+//    case when a chunk of a sequence is written) it stores them as one 16-byte
+//    unit of the page, otherwise (scattered tokens, e.g. one new token per
+//    sequence) one element per token.
 template <int ESIZE>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const uint8_t* __restrict__ key, const uint8_t* __restrict__ value, uint8_t* __restrict__ kc,
@@ -45,58 +47,53 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   const int64_t my_slot = lane < ntok ? slots[tok0 + lane] : -1;
 
   if (threadIdx.x < 128) {
-    // ---- keys (X * nchunk <= 128 units)
-    for (int u = threadIdx.x; u < X * nchunk; u += 128) {
-      const int j = u / nchunk, c = u - (u / nchunk) * nchunk;
-      const int64_t slot = __shfl(my_slot, j, 64);
-      if (j < ntok && slot >= 0) {
-        const int64_t blk = slot / block_size;
-        const int off = static_cast<int>(slot % block_size);
-        const uint4 v = *reinterpret_cast<const uint4*>(
-            key + (tok0 + j) * kstride_bytes + static_cast<int64_t>(head) * head_dim * ESIZE +
-            c * 16);
-        *reinterpret_cast<uint4*>(
-            kc + ((((blk * kvh + head) * nchunk + c) * block_size) + off) * 16) = v;
-      }
+    // ---- keys (X * nchunk <= 128 units: one per thread at most)
+    const int u = threadIdx.x;
+    const int j = u / nchunk, c = u - (u / nchunk) * nchunk;
+    const bool have = u < X * nchunk && j < ntok;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (have)
+      v = *reinterpret_cast<const uint4*>(key + (tok0 + j) * kstride_bytes +
+                                          static_cast<int64_t>(head) * head_dim * ESIZE + c * 16);
+    const int64_t slot = __shfl(my_slot, j < X ? j : 0, 64);
+    if (have && slot >= 0) {
+      const int64_t blk = slot / block_size;
+      const int off = static_cast<int>(slot % block_size);
+      *reinterpret_cast<uint4*>(kc + ((((blk * kvh + head) * nchunk + c) * block_size) + off) * 16) =
+          v;
     }
     return;
   }
 
-  // ---- values
-  const int vt = threadIdx.x - 128;
+  // ---- values (head_dim <= 128: one dimension per thread at most)
+  const int d = threadIdx.x - 128;
+  elem_t e[X];
+#pragma unroll
+  for (int j = 0; j < X; ++j) {
+    e[j] = 0;
+    if (d < head_dim && j < ntok)
+      e[j] = reinterpret_cast<const elem_t*>(value + (tok0 + j) * vstride_bytes)
+          [static_cast<int64_t>(head) * head_dim + d];
+  }
   const int64_t s0 = __shfl(my_slot, 0, 64);
   const bool run = ntok == X && s0 >= 0 && s0 % X == 0 &&
                    __all(lane >= X || my_slot == s0 + lane);
+  if (d >= head_dim) return;
   if (run) {
     const int64_t blk = s0 / block_size;
     const int off = static_cast<int>(s0 % block_size);
     elem_t* vpage = reinterpret_cast<elem_t*>(vc) + (blk * kvh + head) * head_dim * block_size + off;
-    for (int d = vt; d < head_dim; d += 128) {
-      elem_t e[X];
-#pragma unroll
-      for (int j = 0; j < X; ++j)
-        e[j] = reinterpret_cast<const elem_t*>(value + (tok0 + j) * vstride_bytes)
-            [static_cast<int64_t>(head) * head_dim + d];
-      *reinterpret_cast<uint4*>(vpage + static_cast<int64_t>(d) * block_size) =
-          __builtin_bit_cast(uint4, e);
-    }
+    *reinterpret_cast<uint4*>(vpage + static_cast<int64_t>(d) * block_size) =
+        __builtin_bit_cast(uint4, e);
   } else {
-    for (int d = vt; d < head_dim; d += 128) {
-      elem_t e[X];
 #pragma unroll
-      for (int j = 0; j < X; ++j)
-        if (j < ntok)
-          e[j] = reinterpret_cast<const elem_t*>(value + (tok0 + j) * vstride_bytes)
-              [static_cast<int64_t>(head) * head_dim + d];
-#pragma unroll
-      for (int j = 0; j < X; ++j) {
-        const int64_t slot = __shfl(my_slot, j, 64);
-        if (j < ntok && slot >= 0) {
-          const int64_t blk = slot / block_size;
-          const int off = static_cast<int>(slot % block_size);
-          reinterpret_cast<elem_t*>(vc)[(blk * kvh + head) * head_dim * block_size +
-                                        static_cast<int64_t>(d) * block_size + off] = e[j];
-        }
+    for (int j = 0; j < X; ++j) {
+      const int64_t slot = __shfl(my_slot, j, 64);
+      if (j < ntok && slot >= 0) {
+        const int64_t blk = slot / block_size;
+        const int off = static_cast<int>(slot % block_size);
+        reinterpret_cast<elem_t*>(vc)[(blk * kvh + head) * head_dim * block_size +
+                                      static_cast<int64_t>(d) * block_size + off] = e[j];
       }
     }
   }
