@@ -54,9 +54,13 @@ def blocks_read_once(tables, groups=None, pre=None, block_size: int = 16) -> boo
     t = np.asarray(tables)
     read = t >= 0
     if groups is not None and len(groups):
-        skip = np.zeros(t.shape[0], dtype=np.int64)   # leading columns not read per row
-        for first, n, _ in groups:
-            skip[first + 1:first + n] = pre[first + 1:first + n] // block_size
+        g = np.asarray(groups, dtype=np.int64).reshape(-1, 3)
+        # rows after each group's first: their prefix columns are not read
+        marks = np.zeros(t.shape[0] + 1, dtype=np.int64)
+        np.add.at(marks, g[:, 0] + 1, 1)
+        np.add.at(marks, g[:, 0] + g[:, 1], -1)
+        member = np.cumsum(marks)[:-1] > 0
+        skip = np.where(member, np.asarray(pre, dtype=np.int64) // block_size, 0)
         read &= np.arange(t.shape[1])[None, :] >= skip[:, None]
     ids = t[read]
     return ids.size == 0 or int(np.bincount(ids).max()) <= 1
@@ -72,31 +76,29 @@ def found_groups(tables, lens, run: int = 8, min_prefix: int = 256, block_size: 
     length per sequence)."""
     t = np.asarray(tables)
     lens = np.asarray(lens)
-    B = t.shape[0]
+    B, mb = t.shape
     whole = lens // block_size
     pre = np.zeros(B, np.int32)
     firsts = np.arange(0, B, run)
-    P = whole[firsts].astype(np.int64)           # candidate prefix per run, blocks
-    count = np.ones(len(firsts), np.int64)
-    alive = np.ones(len(firsts), bool)
+    # every candidate member's first block id differing from its leader's
+    idx = firsts[:, None] + np.arange(1, run)[None, :]
+    valid = idx < B
+    idx = np.minimum(idx, B - 1)
+    diff = t[idx] != t[firsts][:, None, :]
+    first_diff = np.where(diff.any(2), diff.argmax(2), mb)
+    # Member m joins while every earlier one did and, with the prefix cut to
+    # what it shares, the prefix stays >= min_prefix and the reads saved do
+    # not fall: the prefix after member m would be the running minimum.
     floor_min = max(min_prefix, block_size)
-    cols = np.arange(t.shape[1])
-    for m in range(1, run):
-        s = firsts + m
-        ok = alive & (s < B)
-        if not ok.any():
-            break
-        r = np.nonzero(ok)[0]
-        lead, other = t[firsts[r]], t[s[r]]
-        limit = np.minimum(P[r], whole[s[r]])
-        diff = (lead != other) & (cols[None, :] < limit[:, None])
-        common = np.where(diff.any(1), diff.argmax(1), limit)
-        join = (common * block_size >= floor_min) & (common * count[r] >= P[r] * (count[r] - 1))
-        alive[r[~join]] = False
-        jr = r[join]
-        P[jr] = common[join]
-        count[jr] += 1
-        alive &= s < B
+    c = np.minimum(first_diff, whole[idx]).astype(np.int64)
+    P0 = whole[firsts].astype(np.int64)[:, None]
+    Pc = np.minimum(P0, np.minimum.accumulate(c, axis=1))     # prefix once member m is in
+    Pprev = np.concatenate([P0, Pc[:, :-1]], axis=1)
+    m = np.arange(1, run)[None, :]                            # group size before member m
+    cond = valid & (Pc * block_size >= floor_min) & (Pc * m >= Pprev * (m - 1))
+    joined = np.cumprod(cond, axis=1).sum(1)
+    count = 1 + joined
+    P = Pc[np.arange(len(firsts)), np.maximum(joined - 1, 0)]
     groups = []
     for i, first in enumerate(firsts):
         if count[i] >= 2:
